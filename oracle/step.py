@@ -1,0 +1,176 @@
+"""One rank's local optimizer step: pack, sum of squares, clip, AdamW, bf16
+cast, unpack. Plain numpy, float64 arithmetic.
+
+Sources (pages, not code):
+  * "第 5 课：ZeRO 与 FSDP", section 3 (ZeRO-1/2 step 2): each rank updates its
+    own 1/N_d slice of the fp32 optimizer state and master weights with its own
+    gradient slice and converts the result to BF16 in place; the all-gather
+    then reassembles the full parameters. Section 2: K = 12 bytes of state per
+    parameter (fp32 master, m, v). Section 3 (ZeRO-3): the optimizer update
+    needs no communication.
+  * "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
+    (notes): section 2.2 (tensors are flattened and fused into a contiguous
+    buffer for the gradient norm), section 3.2.3 (tensors are copied into
+    pre-allocated contiguous blocks as they are produced), section 4.1 (rank i
+    reads only its slice of the gradient and updates only its slice; an
+    all-gather then restores the full 16-bit parameters).
+  * "ZeRO-3 核心流程：把参数也切开的那一档", pitfall 1: gradient clipping must
+    use the norm over all ranks' slices, not each rank's own.
+
+Readings where the pages are silent (the pages print no optimizer equations,
+no clipping formula and no rounding mode):
+  * AdamW as PyTorch's ``torch.optim.AdamW`` computes it (decoupled weight
+    decay scaled by lr, bias-corrected moments, eps added outside the square
+    root), applied to every element of the flat shard.
+  * Clipping as ``torch.nn.utils.clip_grad_norm_`` computes it, on the global
+    L2 norm: c = max_norm / (norm + clip_eps), kept only when below 1; a
+    max_norm <= 0 turns clipping off. c scales the gradient before the
+    moments. A NaN norm gives a NaN coefficient (it is not clamped to 1).
+  * The global sum of squares is the sum of the per-rank partial sums taken in
+    rank order.
+  * m, v and the master weight are stored as fp32 (round to nearest even)
+    after every step; the bf16 parameter is the bf16 rounding of the stored
+    fp32 master.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from .bf16 import bf16_to_f32, f32_to_bf16
+
+CHUNK = 1 << 22   # elements per piece: temporaries stay a constant size
+
+
+@dataclass(frozen=True)
+class AdamWHParams:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    max_norm: float = 1.0
+    clip_eps: float = 1e-6
+
+
+# ---------------------------------------------------------------- pack/unpack
+
+def pack(layout, tensors, begin: int = 0, count: int | None = None) -> np.ndarray:
+    """Shard elements [begin, begin+count) gathered from the per-tensor bf16
+    gradients. Padding elements are 0. ``tensors[i]`` is tensor i's full
+    uint16 array (or None when no segment of the range touches it)."""
+    if count is None:
+        count = layout.shard - begin
+    if begin < 0 or count < 0 or begin + count > layout.shard:
+        raise ValueError("range outside the shard")
+    out = np.zeros(count, dtype=np.uint16)
+    end = begin + count
+    for seg in layout.segments:
+        lo = max(seg.dst_off, begin)
+        hi = min(seg.dst_off + seg.length, end)
+        if lo >= hi:
+            continue
+        src = np.asarray(tensors[seg.tensor], dtype=np.uint16)
+        s0 = seg.src_off + (lo - seg.dst_off)
+        out[lo - begin:hi - begin] = src[s0:s0 + (hi - lo)]
+    return out
+
+
+def unpack(layout, shard_bits, tensors, begin: int = 0, count: int | None = None):
+    """Copies of ``tensors`` with the elements that shard range
+    [begin, begin+count) owns overwritten from ``shard_bits`` (which holds that
+    range). Padding goes nowhere; nothing else changes."""
+    if count is None:
+        count = layout.shard - begin
+    if begin < 0 or count < 0 or begin + count > layout.shard:
+        raise ValueError("range outside the shard")
+    shard_bits = np.asarray(shard_bits, dtype=np.uint16)
+    out = [None if t is None else np.array(t, dtype=np.uint16, copy=True) for t in tensors]
+    end = begin + count
+    for seg in layout.segments:
+        lo = max(seg.dst_off, begin)
+        hi = min(seg.dst_off + seg.length, end)
+        if lo >= hi:
+            continue
+        d0 = seg.src_off + (lo - seg.dst_off)
+        out[seg.tensor][d0:d0 + (hi - lo)] = shard_bits[lo - begin:hi - begin]
+    return out
+
+
+# ------------------------------------------------------------ sum of squares
+
+def sqnorm(grad_bits) -> float:
+    """Sum of squares of a bf16 gradient range, in float64. Each square of a
+    bf16 value is exact in float64."""
+    g = np.asarray(grad_bits, dtype=np.uint16).reshape(-1)
+    total = 0.0
+    for lo in range(0, g.size, CHUNK):
+        x = bf16_to_f32(g[lo:lo + CHUNK]).astype(np.float64)
+        total += float(np.dot(x, x))
+    return total
+
+
+def global_sqnorm(rank_partials) -> float:
+    """Global sum of squares from the ranks' partial sums, added in rank
+    order (the value an all-reduce of the partials stands for)."""
+    total = 0.0
+    for p in rank_partials:
+        total += float(p)
+    return total
+
+
+def clip_coef(global_sq: float, max_norm: float, clip_eps: float = 1e-6) -> float:
+    """Clip coefficient from the global sum of squares."""
+    if max_norm <= 0:
+        return 1.0
+    ratio = max_norm / (math.sqrt(global_sq) + clip_eps)
+    return 1.0 if ratio >= 1.0 else ratio
+
+
+# ---------------------------------------------------------------------- AdamW
+
+def adamw_f64(p, m, v, g_hat, step: int, hp: AdamWHParams):
+    """One AdamW update in float64 (no storage rounding). ``g_hat`` is the
+    already clipped gradient. Returns (p', m', v')."""
+    if step < 1:
+        raise ValueError("step counts from 1")
+    p = np.asarray(p, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g_hat, dtype=np.float64)
+    m_new = hp.beta1 * m + (1.0 - hp.beta1) * g
+    v_new = hp.beta2 * v + (1.0 - hp.beta2) * (g * g)
+    bias1 = 1.0 - hp.beta1 ** step
+    bias2 = 1.0 - hp.beta2 ** step
+    denom = np.sqrt(v_new) / math.sqrt(bias2) + hp.eps
+    p_new = p * (1.0 - hp.lr * hp.weight_decay) - (hp.lr / bias1) * (m_new / denom)
+    return p_new, m_new, v_new
+
+
+def adamw_step(grad_bits, master, m, v, step: int, hp: AdamWHParams, coef: float):
+    """The rank's fused update over its shard range: scale the bf16 gradient by
+    the clip coefficient, update master/m/v (stored back as fp32) and produce
+    the bf16 parameter shard. Returns (master', m', v', param_bits)."""
+    g_bits = np.asarray(grad_bits, dtype=np.uint16).reshape(-1)
+    master = np.asarray(master, dtype=np.float32).reshape(-1)
+    m = np.asarray(m, dtype=np.float32).reshape(-1)
+    v = np.asarray(v, dtype=np.float32).reshape(-1)
+    n = g_bits.size
+    if not (master.size == m.size == v.size == n):
+        raise ValueError("shard arrays differ in length")
+    out_p = np.empty(n, dtype=np.float32)
+    out_m = np.empty(n, dtype=np.float32)
+    out_v = np.empty(n, dtype=np.float32)
+    out_b = np.empty(n, dtype=np.uint16)
+    for lo in range(0, n, CHUNK):
+        hi = min(n, lo + CHUNK)
+        g_hat = coef * bf16_to_f32(g_bits[lo:hi]).astype(np.float64)
+        p1, m1, v1 = adamw_f64(master[lo:hi], m[lo:hi], v[lo:hi], g_hat, step, hp)
+        out_p[lo:hi] = p1.astype(np.float32)
+        out_m[lo:hi] = m1.astype(np.float32)
+        out_v[lo:hi] = v1.astype(np.float32)
+        out_b[lo:hi] = f32_to_bf16(out_p[lo:hi])
+    return out_p, out_m, out_v, out_b

@@ -1,0 +1,156 @@
+"""Pins for oracle.memory: the pages' printed numbers and stated invariants."""
+
+import json
+import os
+
+import pytest
+
+from oracle import memory
+from oracle.layout import build_layout
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "memory_printed.json")
+
+
+def _golden():
+    with open(GOLDEN, encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _close_to_printed(value, printed, decimals):
+    return abs(value - printed) <= 0.5 * 10.0 ** (-decimals) + 1e-9
+
+
+@pytest.mark.parametrize("case", _golden()["memory"], ids=lambda c: f"{c['psi']:.2g}-nd{c['n_d']}-z{c['stage']}")
+def test_printed_per_rank_memory(case):
+    gb = memory.model_state_bytes(case["psi"], case["n_d"], case["stage"]) / 1e9
+    assert _close_to_printed(gb, case["gb"], case["decimals"]), (case["cite"], gb)
+
+
+@pytest.mark.parametrize("case", _golden()["zero3_with_temporary_full_copy"], ids=lambda c: f"nd{c['n_d']}")
+def test_printed_zero3_peak_with_temporary_copy(case):
+    gb = memory.model_state_bytes(case["psi"], case["n_d"], 3) / 1e9 + case["temporary_gb"]
+    assert _close_to_printed(gb, case["gb"], case["decimals"]), case["cite"]
+    # the temporary full copy is one layer-set of 16-bit params, i.e. 2 Psi here
+    assert case["temporary_gb"] == pytest.approx(2 * case["psi"] / 1e9)
+
+
+@pytest.mark.parametrize("case", _golden()["components_gb"], ids=lambda c: f"{c['psi']:.2g}")
+def test_printed_component_breakdown(case):
+    psi = case["psi"]
+    # recover each component from the stage accounting at N_d = 2: going one
+    # stage up halves exactly one more component
+    z0 = memory.model_state_bytes(psi, 2, 0)
+    z1 = memory.model_state_bytes(psi, 2, 1)
+    z2 = memory.model_state_bytes(psi, 2, 2)
+    z3 = memory.model_state_bytes(psi, 2, 3)
+    optimizer = 2 * (z0 - z1)      # halving the optimizer saved half of it
+    grads = 2 * (z1 - z2)
+    params = 2 * (z2 - z3)
+    assert optimizer / 1e9 == pytest.approx(case["optimizer"]), case["cite"]
+    assert grads / 1e9 == pytest.approx(case["grads"]), case["cite"]
+    assert params / 1e9 == pytest.approx(case["params"]), case["cite"]
+    assert z0 == pytest.approx(params + grads + optimizer)
+
+
+@pytest.mark.parametrize("case", _golden()["per_psi"], ids=lambda c: c["quantity"] + str(c["stage"]))
+def test_printed_per_psi_figures(case):
+    psi = 10**9
+    per = memory.model_state_bytes(psi, case["n_d"], case["stage"]) / psi
+    if case["quantity"] == "total":
+        value = per
+    elif case["quantity"] == "optimizer_share":
+        value = per - memory.model_state_bytes(psi, 10**15, case["stage"]) / psi
+    else:  # saving in percent against the unsharded 16 Psi
+        value = 100.0 * (1.0 - per / (memory.model_state_bytes(psi, 1, 0) / psi))
+    assert _close_to_printed(value, case["value"], case["decimals"]), case["cite"]
+
+
+@pytest.mark.parametrize("case", _golden()["communication"], ids=lambda c: f"z{c['stage']}")
+def test_printed_communication(case):
+    vals = memory.comm_values_pages(case["psi"], case["stage"])
+    assert vals / 1e9 == pytest.approx(case["g_values"]), case["cite"]
+    assert 2 * vals / 1e9 == pytest.approx(case["gb_bf16"]), case["cite"]
+
+
+def test_all_stages_equal_at_one_rank():
+    # the pages' cross-check: with a single rank nothing is divided
+    for psi in (1_000_000, 7_000_000_000, 123):
+        vals = {memory.model_state_bytes(psi, 1, s) for s in range(4)}
+        assert len(vals) == 1
+        vals = {memory.model_state_bytes(psi, 1, s, fp32_grad_accum=True) for s in range(4)}
+        assert len(vals) == 1
+
+
+def test_invalid_arguments_raise():
+    for bad in [(0, 8, 1), (-5, 8, 1), (10, 0, 1), (10, -1, 1), (10, 8, 4), (10, 8, -1)]:
+        with pytest.raises(ValueError):
+            memory.model_state_bytes(*bad)
+    with pytest.raises(ValueError):
+        memory.comm_values_pages(10, 7)
+
+
+def test_fp32_accumulation_follows_gradient_sharding():
+    # stated rule (no printed number): +4 Psi while gradients are replicated
+    # (stages 0, 1), +4 Psi/N_d once they are partitioned (stages 2, 3)
+    psi, n_d = 7_000_000_000, 8
+    for stage, expect in [(0, 4 * psi), (1, 4 * psi), (2, 4 * psi / n_d), (3, 4 * psi / n_d)]:
+        extra = (memory.model_state_bytes(psi, n_d, stage, fp32_grad_accum=True)
+                 - memory.model_state_bytes(psi, n_d, stage))
+        assert extra == pytest.approx(expect)
+
+
+def test_asymptotic_reduction_factors():
+    # about 4x (stage 1), 8x (stage 2) and N_d x (stage 3) less than DDP
+    psi = 10**9
+    big = 10**12
+    z0 = memory.model_state_bytes(psi, big, 0)
+    assert z0 / memory.model_state_bytes(psi, big, 1) == pytest.approx(4.0, rel=1e-9)
+    assert z0 / memory.model_state_bytes(psi, big, 2) == pytest.approx(8.0, rel=1e-9)
+    for n_d in (2, 64, 1024):
+        assert z0 / memory.model_state_bytes(psi, n_d, 3) == pytest.approx(n_d)
+
+
+def test_stage3_is_slope_minus_one():
+    psi = 7_500_000_000
+    for n in (1, 2, 8, 64, 256):
+        assert memory.model_state_bytes(psi, 2 * n, 3) == pytest.approx(
+            memory.model_state_bytes(psi, n, 3) / 2)
+
+
+def test_communication_ratios():
+    psi = 10**9
+    assert memory.comm_values_pages(psi, 1) == memory.comm_values_pages(psi, 0)
+    assert memory.comm_values_pages(psi, 2) == memory.comm_values_pages(psi, 0)
+    assert memory.comm_values_pages(psi, 3) / memory.comm_values_pages(psi, 0) == 1.5
+
+
+def test_layout_accounting_equals_formula_without_padding():
+    # with no padding S = Psi/N_d, so the integer layout accounting must equal
+    # the pages' formula exactly; with padding it exceeds it by < 16 * A bytes
+    # per partitioned byte class (at most 16 B per padded element)
+    for sizes, n_d, align in [([1024] * 8, 4, 128), ([1000, 24], 8, 1),
+                              ([7, 9, 1000], 4, 128), ([33, 1], 3, 5)]:
+        lay = build_layout(sizes, n_d, 0, align)
+        pad_total = lay.padded - lay.psi
+        for stage in range(4):
+            for acc in (False, True):
+                exact = memory.model_state_bytes_layout(lay.psi, lay.shard, stage,
+                                                        fp32_grad_accum=acc)
+                formula = memory.model_state_bytes(lay.psi, n_d, stage, fp32_grad_accum=acc)
+                if pad_total == 0:
+                    assert exact == pytest.approx(formula, rel=0, abs=1e-6)
+                else:
+                    assert 0 <= exact - formula <= 20 * pad_total / n_d + 1e-6
+        # summed over ranks, fully sharded state covers the padded buffer
+        assert n_d * memory.model_state_bytes_layout(lay.psi, lay.shard, 3) == 16 * lay.padded
+
+
+def test_exact_ring_volume_matches_pages_formula_without_padding():
+    # the pages: one reduce-scatter or all-gather moves (N_d - 1)/N_d * Psi
+    psi, n_d = 8 * 128 * 1000, 8
+    lay = build_layout([psi], n_d, 0, 128)
+    assert lay.padded == psi
+    per_pass = (n_d - 1) * psi // n_d
+    assert memory.comm_values_exact(lay.shard, n_d, 1) == 2 * per_pass
+    assert memory.comm_values_exact(lay.shard, n_d, 3) == 3 * per_pass
+    assert memory.comm_values_exact(lay.shard, 1, 3) == 0
