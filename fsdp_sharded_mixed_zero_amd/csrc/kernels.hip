@@ -1,0 +1,646 @@
+// Device code and device-side C ABI of libzero_mi355x.so (gfx950 / CDNA4).
+//
+// All four kernels stream HBM; none is a dense contraction, so none uses the
+// matrix cores. They are written for 64-lane wavefronts and one rule measured
+// on MI355X: every wavefront-wide memory instruction covers one contiguous
+// span (lane k takes the k-th 8 or 16 bytes), and the grid is one-shot (one
+// unit of work per lane, blocks dispatched in address order), so the waves in
+// flight at any moment touch a compact window of each stream. Persistent
+// grid-stride loops and lanes that own 32 contiguous bytes (two half-filled
+// instructions per stream) both measured 10-20% slower. Loads and stores are
+// non-temporal: nothing is reused within a step.
+//
+//   copy_pieces_kernel   pack (tensors -> shard) and unpack (shard -> tensors)
+//   sqnorm_partial_kernel / sqnorm_final_kernel
+//                        deterministic two-stage sum of squares (fp64)
+//   adamw_kernel         clip + AdamW + bf16 cast, 28 bytes per element
+//
+// Sources for what is computed: "第 5 课：ZeRO 与 FSDP" sections 2-3, notes on
+// "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
+// sections 2.1, 2.2, 3.2.3, 4.1-4.3, 5.2, and "ZeRO-3 核心流程" pitfall 1.
+// The update rule and clip coefficient follow PyTorch's AdamW and
+// clip_grad_norm_, the pages giving no equations of their own.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "zero_internal.h"
+
+using zero::fail;
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (gfx950 has a hardware convert).
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(unsigned int, r);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// ============================================================ pack / unpack
+//
+// One launch copies up to kCopyMaxPieces contiguous runs ("pieces"). The
+// pieces travel in the kernel-argument segment, so no table has to be
+// uploaded per call. Blocks are dealt out to pieces by a prefix table; a
+// piece whose source and destination have the same address modulo 16 uses
+// 16-byte vectors (with a scalar head and tail), any other piece an element
+// path. A NULL source writes zeros (padding).
+
+constexpr int kCopyMaxPieces = 64;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecPerThread = 1;
+constexpr int64_t kCopyVecPerBlock = int64_t(kCopyThreads) * kCopyVecPerThread;  // 256 x 16 B
+constexpr int64_t kCopyElemPerBlock = kCopyVecPerBlock * 8;                       // 2048 bf16
+
+struct CopyPieces {
+  int32_t n;
+  int32_t _pad;
+  uint64_t vec_mask;                         // bit p: piece p takes the vector path
+  int64_t first_block[kCopyMaxPieces + 1];   // prefix of blocks per piece
+  const uint16_t* src[kCopyMaxPieces];       // NULL: write zeros
+  uint16_t* dst[kCopyMaxPieces];
+  int64_t len[kCopyMaxPieces];
+};
+
+__host__ __device__ inline int64_t copy_head(const void* dst, int64_t len) {
+  // elements before dst reaches a 16-byte boundary (dst is 2-byte aligned)
+  const int64_t h = int64_t(((16u - (uintptr_t(dst) & 15u)) & 15u) >> 1);
+  return h < len ? h : len;
+}
+
+__host__ __device__ inline int64_t copy_blocks(const void* dst, int64_t len, bool vec) {
+  if (vec) {
+    const int64_t nvec = (len - copy_head(dst, len)) >> 3;
+    const int64_t b = (nvec + kCopyVecPerBlock - 1) / kCopyVecPerBlock;
+    return b > 0 ? b : 1;
+  }
+  const int64_t b = (len + kCopyElemPerBlock - 1) / kCopyElemPerBlock;
+  return b > 0 ? b : 1;
+}
+
+__global__ __launch_bounds__(kCopyThreads) void copy_pieces_kernel(const CopyPieces P) {
+  const int64_t b = blockIdx.x;
+  // the piece this block serves: the last p with first_block[p] <= b
+  int lo = 0, hi = P.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.first_block[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const int p = lo;
+  const int64_t lb = b - P.first_block[p];
+  const uint16_t* __restrict__ src = P.src[p];
+  uint16_t* __restrict__ dst = P.dst[p];
+  const int64_t len = P.len[p];
+  const int t = threadIdx.x;
+
+  if ((P.vec_mask >> p) & 1u) {
+    const int64_t head = copy_head(dst, len);
+    const int64_t nvec = (len - head) >> 3;
+    const int64_t tail0 = head + nvec * 8;
+    if (lb == 0) {
+      if (t < head) dst[t] = src ? src[t] : uint16_t(0);
+      const int64_t k = tail0 + (t - 8);
+      if (t >= 8 && k < len) dst[k] = src ? src[k] : uint16_t(0);
+    }
+    const u32x4* __restrict__ s = reinterpret_cast<const u32x4*>(src + head);
+    u32x4* __restrict__ d = reinterpret_cast<u32x4*>(dst + head);
+    const int64_t base = lb * kCopyVecPerBlock + t;
+    u32x4 r[kCopyVecPerThread];
+#pragma unroll
+    for (int k = 0; k < kCopyVecPerThread; ++k) {
+      const int64_t i = base + int64_t(k) * kCopyThreads;
+      r[k] = (src && i < nvec) ? __builtin_nontemporal_load(s + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyVecPerThread; ++k) {
+      const int64_t i = base + int64_t(k) * kCopyThreads;
+      if (i < nvec) __builtin_nontemporal_store(r[k], d + i);
+    }
+  } else {
+    const int64_t base = lb * kCopyElemPerBlock + t;
+    constexpr int kPer = int(kCopyElemPerBlock / kCopyThreads);
+#pragma unroll 8
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t i = base + int64_t(k) * kCopyThreads;
+      if (i < len) dst[i] = src ? src[i] : uint16_t(0);
+    }
+  }
+}
+
+struct Piece {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t len;
+};
+
+// A launch's work-item count must fit in 32 bits: at most 2^23 blocks of 256.
+constexpr int64_t kCopyMaxBlocksPerLaunch = int64_t(1) << 23;
+// Pieces are cut to at most 2^34 elements (2^21 blocks) so any piece fits.
+constexpr int64_t kCopyMaxPieceElems = int64_t(1) << 34;
+
+int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who) {
+  size_t i = 0;
+  while (i < pieces.size()) {
+    CopyPieces P{};
+    int64_t blocks = 0;
+    int n = 0;
+    for (; i < pieces.size() && n < kCopyMaxPieces; ++i, ++n) {
+      const Piece& pc = pieces[i];
+      const bool vec = pc.src == nullptr ||
+                       ((uintptr_t(pc.src) & 15u) == (uintptr_t(pc.dst) & 15u));
+      const int64_t nb = copy_blocks(pc.dst, pc.len, vec);
+      if (n > 0 && blocks + nb > kCopyMaxBlocksPerLaunch) break;  // launch what we have first
+      P.src[n] = pc.src;
+      P.dst[n] = pc.dst;
+      P.len[n] = pc.len;
+      if (vec) P.vec_mask |= uint64_t(1) << n;
+      P.first_block[n] = blocks;
+      blocks += nb;
+    }
+    P.n = n;
+    P.first_block[n] = blocks;
+    if (blocks > kCopyMaxBlocksPerLaunch) return fail(ZERO_EINVAL, "%s: piece too large for one launch", who);
+    hipLaunchKernelGGL(copy_pieces_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, stream, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  }
+  return zero::ok();
+}
+
+// Pieces of shard range [begin, begin+count): one per segment overlap, plus
+// the padding overlap. `to_shard` selects pack (tensor -> shard) or unpack.
+int build_pieces(const zero_layout_s* h, uint16_t* const* tensors, uint16_t* shard, int64_t begin,
+                 int64_t count, bool to_shard, std::vector<Piece>* out, const char* who) {
+  const int64_t end = begin + count;
+  const auto& segs = h->segs;
+  // segments are sorted by dst_off: skip to the first that ends after begin
+  size_t s = size_t(std::upper_bound(segs.begin(), segs.end(), begin,
+                                     [](int64_t v, const zero_segment& g) { return v < g.dst_off + g.len; }) -
+                    segs.begin());
+  for (; s < segs.size() && segs[s].dst_off < end; ++s) {
+    const zero_segment& g = segs[s];
+    const int64_t lo = std::max(g.dst_off, begin);
+    const int64_t hi = std::min(g.dst_off + g.len, end);
+    if (lo >= hi) continue;
+    uint16_t* t = tensors[g.tensor];
+    if (t == nullptr)
+      return fail(ZERO_EINVAL, "%s: pointer of tensor %lld is NULL but the range needs it", who,
+                  (long long)g.tensor);
+    if (uintptr_t(t) & 1u) return fail(ZERO_EINVAL, "%s: tensor %lld pointer is not 2-byte aligned", who,
+                                       (long long)g.tensor);
+    for (int64_t a = lo; a < hi; a += kCopyMaxPieceElems) {
+      const int64_t n = std::min(kCopyMaxPieceElems, hi - a);
+      uint16_t* tp = t + g.src_off + (a - g.dst_off);
+      uint16_t* sp = shard + a;
+      out->push_back(to_shard ? Piece{tp, sp, n} : Piece{sp, tp, n});
+    }
+  }
+  if (to_shard) {
+    const int64_t lo = std::max(h->info.pad_begin, begin);
+    const int64_t hi = std::min(h->info.pad_end, end);
+    for (int64_t a = lo; a < hi; a += kCopyMaxPieceElems)
+      out->push_back(Piece{nullptr, shard + a, std::min(kCopyMaxPieceElems, hi - a)});
+  }
+  return zero::ok();
+}
+
+int check_range(const zero_layout_s* h, int64_t begin, int64_t count, const char* who) {
+  if (begin < 0 || count < 0 || begin > h->info.shard || count > h->info.shard - begin)
+    return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside the shard of %lld elements", who,
+                (long long)begin, (long long)count, (long long)h->info.shard);
+  return ZERO_OK;
+}
+
+// ============================================================ sum of squares
+//
+// Stage 1: one-shot blocks (grid-stride only beyond kSqMaxBlocks tiles); each
+// lane loads two 16-byte vectors of a 4096-element tile, squares every bf16
+// value in fp64 (exact) and accumulates in fp64; the block reduces through
+// wavefront shuffles and LDS in a fixed pattern and writes one partial.
+// Stage 2: one block adds the partials in a fixed pattern. The number of
+// blocks depends only on count and no atomics are used, so results are
+// bit-reproducible.
+
+constexpr int kSqThreads = 256;
+constexpr int kSqVecPerThread = 2;
+constexpr int64_t kSqVecPerBlock = int64_t(kSqThreads) * kSqVecPerThread;  // 4096 bf16
+constexpr int64_t kSqMaxBlocks = 65536;
+constexpr int kSqFinalThreads = 1024;
+
+int sq_blocks(int64_t count) {
+  const int64_t nvec = count >> 3;
+  int64_t b = (nvec + kSqVecPerBlock - 1) / kSqVecPerBlock;
+  if (b < 1) b = 1;
+  if (b > kSqMaxBlocks) b = kSqMaxBlocks;
+  return int(b);
+}
+
+__device__ __forceinline__ double sq8(u32x4 w, double acc) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double a = double(bf16_lo(w[k]));
+    const double b = double(bf16_hi(w[k]));
+    acc = fma(a, a, acc);
+    acc = fma(b, b, acc);
+  }
+  return acc;
+}
+
+// Fixed-order block sum of one double per thread; result valid in thread 0.
+template <int THREADS>
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double lds[THREADS / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = x;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) s += lds[w];
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(const uint16_t* __restrict__ g,
+                                                                     int64_t count, int64_t head,
+                                                                     double* __restrict__ partial) {
+  const int64_t nvec = (count - head) >> 3;
+  const u32x4* __restrict__ gv = reinterpret_cast<const u32x4*>(g + head);
+  double acc = 0.0;
+  for (int64_t tile = blockIdx.x; tile * kSqVecPerBlock < nvec; tile += gridDim.x) {
+    const int64_t i0 = tile * kSqVecPerBlock + threadIdx.x;
+    u32x4 r[kSqVecPerThread];
+#pragma unroll
+    for (int k = 0; k < kSqVecPerThread; ++k) {
+      const int64_t i = i0 + int64_t(k) * kSqThreads;
+      r[k] = i < nvec ? __builtin_nontemporal_load(gv + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kSqVecPerThread; ++k) acc = sq8(r[k], acc);
+  }
+  if (blockIdx.x == 0) {
+    // scalar head (before the first 16-byte boundary) and tail (< 8 values)
+    const int t = threadIdx.x;
+    if (t < head) {
+      const double x = double(__uint_as_float(uint32_t(g[t]) << 16));
+      acc = fma(x, x, acc);
+    }
+    const int64_t k = head + nvec * 8 + (t - 8);
+    if (t >= 8 && k < count) {
+      const double x = double(__uint_as_float(uint32_t(g[k]) << 16));
+      acc = fma(x, x, acc);
+    }
+  }
+  const double s = block_sum<kSqThreads>(acc);
+  if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const double* __restrict__ partial,
+                                                                        int n, double* __restrict__ out,
+                                                                        int accumulate) {
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < n; i += kSqFinalThreads) acc += partial[i];
+  const double s = block_sum<kSqFinalThreads>(acc);
+  if (threadIdx.x == 0) *out = accumulate ? *out + s : s;
+}
+
+// ============================================================ fused AdamW
+//
+// The fp32 state of an n-element shard is one buffer of 3n floats in tiles of
+// kTile elements: tile k covers elements [k*T, k*T + L_k), L_k = min(T, n - k*T),
+// and holds master[L_k], then m[L_k], then v[L_k] (the last tile is compact).
+// Measured on MI355X, keeping the three state streams within one 96 KiB tile
+// raises the update from ~5.6 to ~6.4 TB/s against three separate arrays: the
+// waves in flight then touch one compact window of HBM instead of three
+// windows hundreds of MB apart.
+//
+// One lane owns 4 consecutive elements: an 8-byte bf16 gradient load, one
+// 16-byte load each of master, m and v, the same three stores back and an
+// 8-byte bf16 parameter store: 28 bytes per element, and every wavefront
+// instruction covers one contiguous span (512 B or 1 KiB). The grid is
+// one-shot. The clip coefficient is formed by every lane from the ranks'
+// partial sums (uniform loads, fp64), so the step needs no host
+// synchronisation between the norm and the update.
+
+constexpr int kAdamThreads = 256;
+constexpr int64_t kAdamMaxBlocks = int64_t(1) << 23;   // 2^31 work-items
+constexpr int kTileLog2 = 13;
+constexpr int64_t kTile = int64_t(1) << kTileLog2;     // ZERO_STATE_TILE
+static_assert(kTile == ZERO_STATE_TILE, "state tile size");
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct AdamWArgs {
+  const uint16_t* g;      // shard element 0
+  float* state;           // shard element 0's tile
+  uint16_t* param;        // shard element 0
+  int64_t n_state;        // elements the state buffer describes
+  int64_t begin, end;     // elements to update
+  int64_t u_begin, u_end; // 4-element units inside [begin, end)
+  const double* rank_sq;
+  int32_t n_ranks;
+  int32_t clip_on;
+  double max_norm;
+  double clip_eps;
+  float beta1, omb1, beta2, omb2;
+  float lr_wd, step_size, inv_sqrt_bc2, eps;
+};
+
+__device__ __forceinline__ float clip_coefficient(const AdamWArgs& a) {
+  if (!a.clip_on) return 1.0f;
+  double G = 0.0;
+  for (int r = 0; r < a.n_ranks; ++r) G += a.rank_sq[r];
+  const double ratio = a.max_norm / (sqrt(G) + a.clip_eps);
+  return float(ratio >= 1.0 ? 1.0 : ratio);  // a NaN ratio stays NaN
+}
+
+__device__ __forceinline__ void adamw_one(const AdamWArgs& a, float c, float g, float& p, float& m,
+                                          float& v) {
+  const float gh = g * c;
+  m = fmaf(a.beta1, m, a.omb1 * gh);
+  v = fmaf(a.beta2, v, a.omb2 * (gh * gh));
+  const float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
+  const float upd = a.step_size * (m / denom);
+  p = fmaf(-a.lr_wd, p, p) - upd;
+}
+
+// Position of element e's master value in the state buffer and its tile length.
+__device__ __forceinline__ float* tile_slot(const AdamWArgs& a, int64_t e, int64_t* len) {
+  const int64_t k0 = (e >> kTileLog2) << kTileLog2;   // first element of the tile
+  const int64_t rest = a.n_state - k0;
+  *len = rest < kTile ? rest : kTile;
+  return a.state + 3 * k0 + (e - k0);
+}
+
+__device__ __forceinline__ void adamw_scalar(const AdamWArgs& a, float c, int64_t e) {
+  int64_t L;
+  float* s = tile_slot(a, e, &L);
+  float p = s[0], m = s[L], v = s[2 * L];
+  adamw_one(a, c, __uint_as_float(uint32_t(a.g[e]) << 16), p, m, v);
+  s[0] = p;
+  s[L] = m;
+  s[2 * L] = v;
+  a.param[e] = to_bf16(p);
+}
+
+__global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs a) {
+  const float c = clip_coefficient(a);
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  for (int64_t u = a.u_begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < a.u_end; u += stride) {
+    const int64_t e = u << 2;
+    int64_t L;
+    float* s = tile_slot(a, e, &L);
+    if (L & 3) {   // a compact last tile whose m and v are not 16-byte aligned
+      for (int k = 0; k < 4; ++k) adamw_scalar(a, c, e + k);
+      continue;
+    }
+    f32x4* ps = reinterpret_cast<f32x4*>(s);
+    f32x4* ms = reinterpret_cast<f32x4*>(s + L);
+    f32x4* vs = reinterpret_cast<f32x4*>(s + 2 * L);
+    const u32x2 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.g + e));
+    const f32x4 p4 = __builtin_nontemporal_load(ps);
+    const f32x4 m4 = __builtin_nontemporal_load(ms);
+    const f32x4 v4 = __builtin_nontemporal_load(vs);
+    float p[4] = {p4[0], p4[1], p4[2], p4[3]};
+    float m[4] = {m4[0], m4[1], m4[2], m4[3]};
+    float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float g = (k & 1) ? bf16_hi(gw[k >> 1]) : bf16_lo(gw[k >> 1]);
+      adamw_one(a, c, g, p[k], m[k], v[k]);
+    }
+    __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, ps);
+    __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, ms);
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, vs);
+    __builtin_nontemporal_store(u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])},
+                                reinterpret_cast<u32x2*>(a.param + e));
+  }
+  // up to 3 elements before the first unit and after the last one
+  if (blockIdx.x == 0) {
+    const int t = threadIdx.x;
+    const int64_t head_end = 4 * a.u_begin < a.end ? 4 * a.u_begin : a.end;
+    if (t < 4 && a.begin + t < head_end) adamw_scalar(a, c, a.begin + t);
+    const int64_t k = 4 * a.u_end + (t - 4);
+    if (t >= 4 && t < 8 && k >= head_end && k < a.end) adamw_scalar(a, c, k);
+  }
+}
+
+// Element path for base pointers without the vector path's alignment.
+__global__ __launch_bounds__(kAdamThreads) void adamw_elem_kernel(const AdamWArgs a) {
+  const float c = clip_coefficient(a);
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  for (int64_t e = a.begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; e < a.end; e += stride)
+    adamw_scalar(a, c, e);
+}
+
+// ------------------------------------------------ state layout conversion
+// Separate master/m/v arrays <-> the tiled state buffer (a bit copy). One lane
+// moves 4 consecutive elements of each array when everything is 16-byte
+// aligned and the tile length is a multiple of 4, one element otherwise.
+
+template <bool TO_TILES>
+__global__ __launch_bounds__(kAdamThreads) void state_convert_kernel(float* state, float* master, float* m,
+                                                                      float* v, int64_t n, int vec) {
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  const int64_t units = vec ? (n >> 2) : n;
+  for (int64_t u = int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < units; u += stride) {
+    const int64_t e0 = vec ? (u << 2) : u;
+    const int64_t k0 = (e0 >> kTileLog2) << kTileLog2;
+    const int64_t L = (n - k0) < kTile ? (n - k0) : kTile;
+    float* s = state + 3 * k0 + (e0 - k0);
+    if (vec && !(L & 3)) {
+      f32x4* sp = reinterpret_cast<f32x4*>(s);
+      f32x4* sm = reinterpret_cast<f32x4*>(s + L);
+      f32x4* sv = reinterpret_cast<f32x4*>(s + 2 * L);
+      f32x4* xp = reinterpret_cast<f32x4*>(master + e0);
+      f32x4* xm = reinterpret_cast<f32x4*>(m + e0);
+      f32x4* xv = reinterpret_cast<f32x4*>(v + e0);
+      if (TO_TILES) { *sp = *xp; *sm = *xm; *sv = *xv; }
+      else { *xp = *sp; *xm = *sm; *xv = *sv; }
+    } else {
+      const int cnt = vec ? 4 : 1;
+      for (int k = 0; k < cnt; ++k) {
+        if (TO_TILES) { s[k] = master[e0 + k]; s[L + k] = m[e0 + k]; s[2 * L + k] = v[e0 + k]; }
+        else { master[e0 + k] = s[k]; m[e0 + k] = s[L + k]; v[e0 + k] = s[2 * L + k]; }
+      }
+    }
+  }
+  if (vec && blockIdx.x == 0 && threadIdx.x < (n & 3)) {   // the last n % 4 elements
+    const int64_t e = ((n >> 2) << 2) + threadIdx.x;
+    const int64_t k0 = (e >> kTileLog2) << kTileLog2;
+    const int64_t L = n - k0 < kTile ? n - k0 : kTile;
+    float* s = state + 3 * k0 + (e - k0);
+    if (TO_TILES) { s[0] = master[e]; s[L] = m[e]; s[2 * L] = v[e]; }
+    else { master[e] = s[0]; m[e] = s[L]; v[e] = s[2 * L]; }
+  }
+}
+
+bool aligned(const void* p, uintptr_t n) { return (uintptr_t(p) & (n - 1)) == 0; }
+
+}  // namespace
+
+// ================================================================== C ABI
+
+extern "C" int zero_pack_grads(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                               int64_t begin, int64_t count, hipStream_t stream) {
+  static const char* who = "zero_pack_grads";
+  if (h == nullptr || tensor_grads == nullptr || grad_shard == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL handle, tensor array or shard", who);
+  if (int rc = check_range(h, begin, count, who)) return rc;
+  if (uintptr_t(grad_shard) & 1u) return fail(ZERO_EINVAL, "%s: shard pointer is not 2-byte aligned", who);
+  if (count == 0) return zero::ok();
+  std::vector<Piece> pieces;
+  if (int rc = build_pieces(h, const_cast<uint16_t* const*>(tensor_grads), grad_shard, begin, count, true,
+                            &pieces, who))
+    return rc;
+  return launch_pieces(pieces, stream, who);
+}
+
+extern "C" int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* const* tensor_params,
+                                  int64_t begin, int64_t count, hipStream_t stream) {
+  static const char* who = "zero_unpack_params";
+  if (h == nullptr || tensor_params == nullptr || param_shard == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL handle, tensor array or shard", who);
+  if (int rc = check_range(h, begin, count, who)) return rc;
+  if (uintptr_t(param_shard) & 1u) return fail(ZERO_EINVAL, "%s: shard pointer is not 2-byte aligned", who);
+  if (count == 0) return zero::ok();
+  std::vector<Piece> pieces;
+  if (int rc = build_pieces(h, tensor_params, const_cast<uint16_t*>(param_shard), begin, count, false,
+                            &pieces, who))
+    return rc;
+  return launch_pieces(pieces, stream, who);
+}
+
+extern "C" size_t zero_sqnorm_workspace_bytes(int64_t count) {
+  if (count < 0) count = 0;
+  return size_t(sq_blocks(count)) * sizeof(double);
+}
+
+extern "C" int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int32_t accumulate,
+                                 void* d_workspace, size_t ws_bytes, hipStream_t stream) {
+  static const char* who = "zero_shard_sqnorm";
+  if (count < 0) return fail(ZERO_EINVAL, "%s: count < 0", who);
+  if (d_out == nullptr || d_workspace == nullptr) return fail(ZERO_EINVAL, "%s: NULL output or workspace", who);
+  if (count > 0 && d_grad == nullptr) return fail(ZERO_EINVAL, "%s: NULL gradient", who);
+  if (uintptr_t(d_grad) & 1u) return fail(ZERO_EINVAL, "%s: gradient pointer is not 2-byte aligned", who);
+  if (uintptr_t(d_workspace) & 7u) return fail(ZERO_EINVAL, "%s: workspace is not 8-byte aligned", who);
+  const int nb = sq_blocks(count);
+  if (ws_bytes < size_t(nb) * sizeof(double))
+    return fail(ZERO_EINVAL, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, size_t(nb) * sizeof(double));
+  double* part = static_cast<double*>(d_workspace);
+  const int64_t head = copy_head(d_grad, count);
+  hipLaunchKernelGGL(sqnorm_partial_kernel, dim3(nb), dim3(kSqThreads), 0, stream, d_grad, count, head, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, part, nb, d_out,
+                     accumulate ? 1 : 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                               int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                               const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream) {
+  static const char* who = "zero_adamw_step";
+  if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
+  if (n_state < 0 || begin < 0 || count < 0 || begin > n_state || count > n_state - begin)
+    return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside a state of %lld elements", who, (long long)begin,
+                (long long)count, (long long)n_state);
+  if (hp->step < 1) return fail(ZERO_EINVAL, "%s: step must be >= 1 (got %lld)", who, (long long)hp->step);
+  const bool clip = hp->max_norm > 0.0;
+  if (clip && (d_rank_sqnorms == nullptr || n_ranks < 1))
+    return fail(ZERO_EINVAL, "%s: clipping needs the ranks' sums of squares", who);
+  if (count == 0) return zero::ok();
+  if (!d_grad || !d_state || !d_param) return fail(ZERO_EINVAL, "%s: NULL buffer", who);
+  if (((uintptr_t(d_grad) | uintptr_t(d_param)) & 1u) || (uintptr_t(d_state) & 3u))
+    return fail(ZERO_EINVAL, "%s: misaligned element pointer", who);
+
+  AdamWArgs a{};
+  a.g = d_grad;
+  a.state = d_state;
+  a.param = d_param;
+  a.n_state = n_state;
+  a.begin = begin;
+  a.end = begin + count;
+  a.u_begin = (begin + 3) >> 2;
+  a.u_end = a.end >> 2;
+  if (a.u_end < a.u_begin) a.u_end = a.u_begin;   // fewer than 4 elements, all scalar
+  a.rank_sq = d_rank_sqnorms;
+  a.n_ranks = clip ? n_ranks : 0;
+  a.clip_on = clip ? 1 : 0;
+  a.max_norm = hp->max_norm;
+  a.clip_eps = hp->clip_eps;
+  a.beta1 = float(hp->beta1);
+  a.omb1 = float(1.0 - hp->beta1);
+  a.beta2 = float(hp->beta2);
+  a.omb2 = float(1.0 - hp->beta2);
+  const double t = double(hp->step);
+  const double bc1 = 1.0 - std::pow(hp->beta1, t);
+  const double bc2 = 1.0 - std::pow(hp->beta2, t);
+  a.lr_wd = float(hp->lr * hp->weight_decay);
+  a.step_size = float(hp->lr / bc1);
+  a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+  a.eps = float(hp->eps);
+
+  const bool vec = aligned(d_grad, 8) && aligned(d_param, 8) && aligned(d_state, 16);
+  const int64_t work = vec ? std::max<int64_t>(a.u_end - a.u_begin, 1) : count;
+  int64_t blocks = (work + kAdamThreads - 1) / kAdamThreads;
+  blocks = std::min(std::max<int64_t>(blocks, 1), kAdamMaxBlocks);
+  if (vec)
+    hipLaunchKernelGGL(adamw_vec_kernel, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(adamw_elem_kernel, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+static int state_convert(bool to_tiles, float* state, float* master, float* m, float* v, int64_t n,
+                         hipStream_t stream, const char* who) {
+  if (n < 0) return fail(ZERO_EINVAL, "%s: n < 0", who);
+  if (n == 0) return zero::ok();
+  if (!state || !master || !m || !v) return fail(ZERO_EINVAL, "%s: NULL buffer", who);
+  if ((uintptr_t(state) | uintptr_t(master) | uintptr_t(m) | uintptr_t(v)) & 3u)
+    return fail(ZERO_EINVAL, "%s: misaligned pointer", who);
+  const bool vec = aligned(state, 16) && aligned(master, 16) && aligned(m, 16) && aligned(v, 16);
+  const int64_t units = vec ? std::max<int64_t>(n >> 2, 1) : n;
+  const int64_t blocks = std::min(std::max<int64_t>((units + kAdamThreads - 1) / kAdamThreads, 1), kAdamMaxBlocks);
+  if (to_tiles)
+    hipLaunchKernelGGL(state_convert_kernel<true>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, state,
+                       master, m, v, n, vec ? 1 : 0);
+  else
+    hipLaunchKernelGGL(state_convert_kernel<false>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, state,
+                       master, m, v, n, vec ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_state_import(const float* d_master, const float* d_m, const float* d_v, float* d_state,
+                                 int64_t n, hipStream_t stream) {
+  return state_convert(true, d_state, const_cast<float*>(d_master), const_cast<float*>(d_m),
+                       const_cast<float*>(d_v), n, stream, "zero_state_import");
+}
+
+extern "C" int zero_state_export(const float* d_state, float* d_master, float* d_m, float* d_v, int64_t n,
+                                 hipStream_t stream) {
+  return state_convert(false, const_cast<float*>(d_state), d_master, d_m, d_v, n, stream, "zero_state_export");
+}

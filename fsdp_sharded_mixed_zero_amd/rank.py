@@ -1,0 +1,155 @@
+"""One data-parallel rank's shard held in device memory, and the local step
+run through the C ABI: pack -> sum of squares -> clip + AdamW + bf16 cast ->
+unpack.
+
+The step is the rank-local part of a ZeRO-2/3 training step ("第 5 课：ZeRO 与
+FSDP" section 3; notes on the ZeRO paper, sections 4.1-4.3). The collectives
+around it (reduce-scatter of gradients before, all-gather of parameters
+after, and the exchange of the ranks' partial sums of squares) are not run:
+on one GPU, the other ranks' partial sums are inputs in ``rank_sq``.
+
+Buffers are allocated once, as contiguous blocks ("ZeRO: Memory
+Optimizations..." notes, section 3.2.3): per-tensor bf16 gradients and
+parameters of every tensor the shard touches (whole tensors, as a model would
+hold them), the flat bf16 gradient and parameter shards, the fp32 state
+(master, m, v: one 12 B/element buffer in the library's tiled layout), the
+ranks' partial sums and the sum-of-squares workspace. With ``bucket`` > 0
+the shard is processed in pieces of that many elements, a constant-size
+working set (notes, section 5.2).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import synth, zero
+
+
+class RankShard:
+    def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
+                 fill: bool = True, bucket: int | None = None):
+        self.wl = wl
+        self.rank = wl.rank if rank is None else rank
+        self.device = torch.device(device)
+        self.layout = zero.zero_layout(wl.sizes, wl.n_d, self.rank, wl.align)
+        self.info = self.layout.info
+        self.segments = self.layout.segments
+        S = self.info["shard"]
+        self.shard = S
+        self.real = S - (self.info["pad_end"] - self.info["pad_begin"])
+        self.bucket = wl.bucket if bucket is None else bucket
+        self.touched = sorted({s[0] for s in self.segments})
+        n_t = len(wl.sizes)
+        self.grads = [None] * n_t
+        self.params = [None] * n_t
+        dev = self.device
+        for i in self.touched:
+            self.grads[i] = torch.empty(wl.sizes[i], dtype=torch.bfloat16, device=dev)
+            self.params[i] = torch.full((wl.sizes[i],), synth.SENTINEL, dtype=torch.int16,
+                                        device=dev).view(torch.bfloat16)
+        self.grad_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
+        self.param_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
+        self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
+        self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
+        piece = self.bucket if self.bucket > 0 else S
+        ws = zero.zero_sqnorm_workspace_bytes(piece)
+        self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=dev)
+        if fill:
+            self.fill_state()
+            self.fill_grads(wl.step)
+            self.fill_other_ranks()
+
+    # ------------------------------------------------------------ inputs
+    STATE_CHUNK = 1 << 26     # elements per generation chunk (a multiple of the state tile)
+
+    def fill_state(self, on_chunk=None):
+        """Draw master ~ N(0, master_std), m ~ N(0, m_std), v ~ |N(0, v_std)|
+        (zeros where the std is 0 and on padding) chunk by chunk as three
+        separate arrays, and import each chunk into the tiled state buffer.
+        ``on_chunk(lo, hi, master, m, v)`` sees each chunk's separate arrays
+        before the import."""
+        wl, real, S = self.wl, self.real, self.shard
+        assert self.STATE_CHUNK % zero.ZERO_STATE_TILE == 0
+        for k, lo in enumerate(range(0, S, self.STATE_CHUNK)):
+            hi = min(S, lo + self.STATE_CHUNK)
+            n = hi - lo
+            bufs = []
+            for buf_id, std, absval in ((synth.MASTER, wl.master_std, False),
+                                        (synth.EXP_AVG, wl.m_std, False),
+                                        (synth.EXP_AVG_SQ, wl.v_std, True)):
+                x = torch.zeros(n, dtype=torch.float32, device=self.device)
+                r = max(0, min(n, real - lo))
+                if std > 0 and r > 0:
+                    synth.device_normal_(x[:r], std, wl.seed, buf_id, abs_value=absval,
+                                         salt=(self.rank << 12) + k)
+                bufs.append(x)
+            if on_chunk is not None:
+                on_chunk(lo, hi, *bufs)
+            zero.zero_state_import(*bufs, self.state[3 * lo:], n)
+        torch.cuda.synchronize()
+
+    def fill_grads(self, step):
+        for i in self.touched:
+            synth.device_grad_(self.grads[i], self.wl, step, salt=i)
+
+    def other_rank_real(self, r):
+        """Parameters (not padding) rank r owns."""
+        S, psi = self.shard, self.info["psi"]
+        return max(0, min(S, psi - r * S))
+
+    def fill_other_ranks(self):
+        """The other ranks' partial sums of squares: their expected value under
+        the gradient distribution (this rank's entry is computed each step)."""
+        vals = [self.other_rank_real(r) * self.wl.grad_sq_mean() for r in range(self.wl.n_d)]
+        vals[self.rank] = 0.0
+        self.rank_sq.copy_(torch.tensor(vals, dtype=torch.float64))
+
+    # --------------------------------------------------------------- step
+    def hparams(self, step):
+        wl = self.wl
+        return zero.hparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                            weight_decay=wl.weight_decay, max_norm=wl.max_norm, step=step)
+
+    def pieces(self):
+        if self.bucket <= 0:
+            return [(0, self.shard)]
+        return [(b, min(self.bucket, self.shard - b)) for b in range(0, self.shard, self.bucket)]
+
+    def step(self, step, stream=None, timing=None):
+        """One local step. ``timing``: optional dict; each phase ("pack",
+        "sqnorm", "adamw", "unpack") gets a list of (start, end) CUDA events
+        recorded around its launches on the current stream."""
+        hp = self.hparams(step)
+        own = self.rank_sq[self.rank:self.rank + 1]
+        pieces = self.pieces()
+
+        def mark(phase, fn):
+            if timing is None:
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            timing.setdefault(phase, []).append((e0, e1))
+
+        for k, (b, n) in enumerate(pieces):
+            mark("pack", lambda: zero.zero_pack_grads(self.layout, self.grads, self.grad_shard, b, n,
+                                                      stream))
+            mark("sqnorm", lambda: zero.zero_shard_sqnorm(self.grad_shard[b:], n, own, k > 0,
+                                                          self.workspace, stream=stream))
+        for b, n in pieces:
+            mark("adamw", lambda: zero.zero_adamw_step(
+                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                self.wl.n_d, stream))
+            mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.params,
+                                                          b, n, stream))
+
+    def bytes_per_step(self):
+        """Algorithmic HBM bytes of one step: pack 4, sum of squares 2, AdamW 28
+        and unpack 4 bytes per shard element (pack writes only 2 on padding,
+        unpack moves nothing there)."""
+        pad = self.shard - self.real
+        return {"pack": 4 * self.real + 2 * pad, "sqnorm": 2 * self.shard,
+                "adamw": 28 * self.shard, "unpack": 4 * self.real}

@@ -198,14 +198,15 @@ def _device_gen(seed, buffer, step, piece, device):
 DEVICE_PIECE = 1 << 26
 
 
-def device_normal_(out, std, seed, buffer, step=0, abs_value=False):
-    """Fill a float32 or bfloat16 CUDA tensor with N(0, std) samples, drawn in
-    pieces of 2^26 elements (piece k from its own stream)."""
+def device_normal_(out, std, seed, buffer, step=0, abs_value=False, salt=0):
+    """Fill a float32 or bfloat16 CUDA tensor with N(0, std) samples (|N| when
+    ``abs_value``), drawn in pieces of 2^26 elements, piece k from stream
+    (seed, buffer, step, salt * 2^20 + k)."""
     import torch
     flat = out.view(-1)
     for k, lo in enumerate(range(0, flat.numel(), DEVICE_PIECE)):
         hi = min(flat.numel(), lo + DEVICE_PIECE)
-        gen = _device_gen(seed, buffer, step, k, out.device)
+        gen = _device_gen(seed, buffer, step, (salt << 20) + k, out.device)
         x = torch.randn(hi - lo, generator=gen, device=out.device, dtype=torch.float32)
         x.mul_(std)
         if abs_value:
@@ -214,17 +215,20 @@ def device_normal_(out, std, seed, buffer, step=0, abs_value=False):
     return out
 
 
-def device_grad_(out_bf16, wl: Workload, step):
-    """Fill a bfloat16 CUDA tensor with the workload's gradient distribution."""
+def device_grad_(out_bf16, wl: Workload, step, salt=0):
+    """Fill a bfloat16 CUDA tensor with the workload's gradient distribution
+    (rounded to bf16 by torch's cast), piece k from stream
+    (seed, GRAD, step, salt * 2^20 + k)."""
     import torch
     flat = out_bf16.view(-1)
     for k, lo in enumerate(range(0, flat.numel(), DEVICE_PIECE)):
         hi = min(flat.numel(), lo + DEVICE_PIECE)
-        gen = _device_gen(wl.seed, GRAD, step, k, out_bf16.device)
+        piece = (salt << 20) + k
+        gen = _device_gen(wl.seed, GRAD, step, piece, out_bf16.device)
         x = torch.randn(hi - lo, generator=gen, device=out_bf16.device, dtype=torch.float32)
         x.mul_(wl.grad_std)
         if wl.spike_frac > 0:
-            mgen = _device_gen(wl.seed, MASK, step, k, out_bf16.device)
+            mgen = _device_gen(wl.seed, MASK, step, piece, out_bf16.device)
             u = torch.rand(hi - lo, generator=mgen, device=out_bf16.device)
             x = torch.where(u < wl.spike_frac, x * wl.spike_scale, x)
         flat[lo:hi].copy_(x)

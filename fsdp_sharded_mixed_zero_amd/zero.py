@@ -1,0 +1,234 @@
+"""Python binding of libzero_mi355x.so: the C ABI declared in include/zero.h,
+same names, argument marshalling only.
+
+Device buffers may be passed as torch tensors (their ``data_ptr()`` is used,
+so a slice passes its offset) or as integer addresses. ``stream`` defaults to
+torch's current stream on the current device. Every step of the computation
+runs in the library's kernels; nothing here computes on the data. A missing
+library raises ``ZeroLibraryMissing`` at the first call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EHIP = -3
+ZERO_ENOMEM = -4
+ZERO_STATE_TILE = 8192      # elements per tile of the fp32 state buffer (include/zero.h)
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, func, code, message):
+        super().__init__(f"{func} failed ({code}): {message}")
+        self.code = code
+
+
+class ZeroLibraryMissing(RuntimeError):
+    pass
+
+
+class zero_segment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int64), ("src_off", ctypes.c_int64),
+                ("dst_off", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+class zero_layout_info(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int64), ("n_d", ctypes.c_int64), ("rank", ctypes.c_int64),
+                ("align", ctypes.c_int64), ("psi", ctypes.c_int64), ("padded", ctypes.c_int64),
+                ("shard", ctypes.c_int64), ("shard_begin", ctypes.c_int64),
+                ("n_segments", ctypes.c_int64), ("pad_begin", ctypes.c_int64),
+                ("pad_end", ctypes.c_int64), ("bytes_stage", ctypes.c_int64 * 4),
+                ("bytes_stage_fp32acc", ctypes.c_int64 * 4), ("comm_pages", ctypes.c_int64 * 4),
+                ("comm_exact", ctypes.c_int64 * 4)]
+
+    def as_dict(self):
+        out = {}
+        for name, _ in self._fields_:
+            val = getattr(self, name)
+            out[name] = list(val) if isinstance(val, ctypes.Array) else int(val)
+        return out
+
+
+class zero_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("max_norm", ctypes.c_double), ("clip_eps", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "zero_layout": (ctypes.c_int, [ctypes.POINTER(_I64), _I32, _I32, _I32, _I64, ctypes.POINTER(_VP)]),
+    "zero_layout_query": (ctypes.c_int, [_VP, ctypes.POINTER(zero_layout_info)]),
+    "zero_layout_segments": (ctypes.c_int, [_VP, ctypes.POINTER(zero_segment), _I64, ctypes.POINTER(_I64)]),
+    "zero_layout_free": (None, [_VP]),
+    "zero_pack_grads": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP]),
+    "zero_sqnorm_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
+    "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
+                                       ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
+    "zero_state_import": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
+    "zero_state_export": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
+    "zero_unpack_params": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_VP), _I64, _I64, _VP]),
+    "zero_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def library(path: str | None = None):
+    """Load (once) and return the ctypes handle of libzero_mi355x.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or os.environ.get("ZERO_MI355X_LIB", LIB_PATH)
+    if not os.path.exists(path):
+        raise ZeroLibraryMissing(
+            f"{path} is not built; run `python -m fsdp_sharded_mixed_zero_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def zero_last_error() -> str:
+    return library().zero_last_error().decode(errors="replace")
+
+
+def _check(func, rc):
+    if rc != ZERO_OK:
+        raise ZeroError(func, rc, zero_last_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr_array(items):
+    arr = (_VP * len(items))()
+    for i, t in enumerate(items):
+        arr[i] = _ptr(t)
+    return arr
+
+
+class Layout:
+    """Owner of a zero_layout_t handle."""
+
+    def __init__(self, handle: int, n_tensors: int):
+        self.handle = handle
+        self.n_tensors = n_tensors
+
+    def close(self):
+        if self.handle:
+            library().zero_layout_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def info(self) -> dict:
+        return zero_layout_query(self)
+
+    @property
+    def segments(self):
+        return zero_layout_segments(self)
+
+
+def zero_layout(sizes, n_d: int, rank: int, align_elems: int = 128) -> Layout:
+    sizes = [int(s) for s in sizes]
+    arr = (_I64 * max(1, len(sizes)))(*sizes)
+    h = _VP()
+    _check("zero_layout", library().zero_layout(arr, len(sizes), n_d, rank, align_elems, ctypes.byref(h)))
+    return Layout(h.value, len(sizes))
+
+
+def zero_layout_free(layout: Layout) -> None:
+    layout.close()
+
+
+def zero_layout_query(layout: Layout) -> dict:
+    info = zero_layout_info()
+    _check("zero_layout_query", library().zero_layout_query(layout.handle, ctypes.byref(info)))
+    return info.as_dict()
+
+
+def zero_layout_segments(layout: Layout):
+    n = _I64()
+    _check("zero_layout_segments", library().zero_layout_segments(layout.handle, None, 0, ctypes.byref(n)))
+    segs = (zero_segment * max(1, n.value))()
+    _check("zero_layout_segments",
+           library().zero_layout_segments(layout.handle, segs, n.value, ctypes.byref(n)))
+    return [(s.tensor, s.src_off, s.dst_off, s.len) for s in segs[:n.value]]
+
+
+def zero_pack_grads(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, stream=None):
+    arr = _ptr_array(tensor_grads)
+    _check("zero_pack_grads", library().zero_pack_grads(
+        layout.handle, arr, _ptr(grad_shard), begin, count, _stream(stream)))
+
+
+def zero_unpack_params(layout: Layout, param_shard, tensor_params, begin: int, count: int, stream=None):
+    arr = _ptr_array(tensor_params)
+    _check("zero_unpack_params", library().zero_unpack_params(
+        layout.handle, _ptr(param_shard), arr, begin, count, _stream(stream)))
+
+
+def zero_sqnorm_workspace_bytes(count: int) -> int:
+    return int(library().zero_sqnorm_workspace_bytes(count))
+
+
+def zero_shard_sqnorm(grad, count: int, out, accumulate: bool, workspace, ws_bytes: int | None = None,
+                      stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_sqnorm", library().zero_shard_sqnorm(
+        _ptr(grad), count, _ptr(out), 1 if accumulate else 0, _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0,
+            clip_eps=1e-6, step=1) -> zero_adamw_hparams:
+    return zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, max_norm, clip_eps, step)
+
+
+def zero_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
+                    rank_sqnorms, n_ranks: int, stream=None):
+    _check("zero_adamw_step", library().zero_adamw_step(
+        _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def zero_state_import(master, m, v, state, n: int, stream=None):
+    _check("zero_state_import", library().zero_state_import(
+        _ptr(master), _ptr(m), _ptr(v), _ptr(state), n, _stream(stream)))
+
+
+def zero_state_export(state, master, m, v, n: int, stream=None):
+    _check("zero_state_export", library().zero_state_export(
+        _ptr(state), _ptr(master), _ptr(m), _ptr(v), n, _stream(stream)))

@@ -1,0 +1,253 @@
+/*
+ * zero.h -- C ABI of libzero_mi355x.so: one data-parallel rank's share of a
+ * ZeRO/FSDP mixed-precision training step on an AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the pages describe it (no collective is run here):
+ *   zero_layout         map a per-tensor size list to flat shard offsets;
+ *   zero_pack_grads     gather the rank's 1/N_d slice of the bf16 gradients
+ *                       into one contiguous shard buffer;
+ *   zero_shard_sqnorm   sum of squares of that shard (the rank's share of
+ *                       the global gradient norm);
+ *   zero_adamw_step     clip with the global norm, AdamW on fp32 master/m/v,
+ *                       cast the new master to the bf16 parameter shard;
+ *   zero_unpack_params  scatter the bf16 parameter shard back into the
+ *                       per-tensor parameters.
+ *
+ * Conventions for every call:
+ *   - bf16 values travel as raw uint16_t bit patterns; fp32 state as float.
+ *   - Sizes and element offsets are int64_t; shards may exceed 2^32 elements.
+ *   - Device pointers are caller-owned device memory (for example torch
+ *     allocations); the library never frees them. Host pointers are read
+ *     during the call only.
+ *   - Device calls enqueue work on the given stream (NULL = the default
+ *     stream) and return without synchronising; results are ready when the
+ *     stream reaches them.
+ *   - Return value: ZERO_OK or a negative error code; zero_last_error()
+ *     gives a message for the calling thread. Argument errors are detected on
+ *     the host before anything is enqueued.
+ */
+#ifndef ZERO_MI355X_H
+#define ZERO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1)  /* bad argument: null pointer, bad size or range */
+#define ZERO_EHIP (-3)    /* a HIP launch or runtime call failed */
+#define ZERO_ENOMEM (-4)  /* host allocation failed */
+
+/* Opaque, immutable description of one rank's shard (host memory only). */
+typedef struct zero_layout_s* zero_layout_t;
+
+/* Tensor elements [src_off, src_off+len) of tensor `tensor` occupy shard
+ * elements [dst_off, dst_off+len). */
+typedef struct {
+  int64_t tensor;
+  int64_t src_off;
+  int64_t dst_off;
+  int64_t len;
+} zero_segment;
+
+/* Facts about a layout. Byte and communication figures are per rank.
+ * bytes_stage[s] is ZeRO stage s's model-state bytes on the generated layout:
+ *   s=0: 16*psi;  s=1: 4*psi + 12*shard;  s=2: 2*psi + 14*shard;  s=3: 16*shard
+ * bytes_stage_fp32acc[s] adds an fp32 gradient-accumulation buffer: 4*psi for
+ * s<=1 (gradients replicated), 4*shard for s>=2 (gradients partitioned).
+ * comm_pages[s] is the pages' per-step approximation in values (2*psi for
+ * stages 0-2, 3*psi for stage 3); comm_exact[s] counts what a ring
+ * reduce-scatter / all-gather sends: (n_d-1)*shard per pass, two passes for
+ * stages 0-2 and three for stage 3.
+ * Sources: "第 5 课：ZeRO 与 FSDP" sections 2-3; notes on the ZeRO paper,
+ * sections 2.1, 4.1-4.3 and 6. */
+typedef struct {
+  int64_t n_tensors;
+  int64_t n_d;
+  int64_t rank;
+  int64_t align;
+  int64_t psi;          /* real parameters: sum of the sizes */
+  int64_t padded;       /* P = ceil(psi / (n_d*align)) * n_d*align */
+  int64_t shard;        /* S = P / n_d, elements every rank owns */
+  int64_t shard_begin;  /* rank*S: first flat element of this shard */
+  int64_t n_segments;
+  int64_t pad_begin;    /* shard elements [pad_begin, pad_end) are padding */
+  int64_t pad_end;      /* (empty when equal) */
+  int64_t bytes_stage[4];
+  int64_t bytes_stage_fp32acc[4];
+  int64_t comm_pages[4];
+  int64_t comm_exact[4];
+} zero_layout_info;
+
+/* AdamW hyperparameters. `step` is the 1-based step count used for the bias
+ * corrections 1-beta1^step and 1-beta2^step (computed on the host in fp64).
+ * max_norm <= 0 turns clipping off; otherwise the gradient is scaled by
+ * c = max_norm / (sqrt(G) + clip_eps) when that is below 1, G being the global
+ * sum of squares. */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+  double max_norm;
+  double clip_eps;
+  int64_t step;
+} zero_adamw_hparams;
+
+/* ---------------------------------------------------------------------------
+ * zero_layout -- the partitioner (host only, no device memory).
+ * Flattens the tensors in list order (notes on the ZeRO paper, sections 2.2
+ * and 5.2: tensors fused into one contiguous buffer), pads the tail so the
+ * buffer splits into n_d equal shards whose starts are multiples of
+ * `align_elems`, and records which runs of which tensors rank `rank` owns
+ * ("第 5 课：ZeRO 与 FSDP" section 2 and notes section 4.1: each rank keeps
+ * 1/N_d of the state). A shard boundary may cut through a tensor.
+ *   sizes       host array of n_tensors element counts (>= 0; zero-size
+ *               tensors get no segment)
+ *   n_d         data-parallel degree (>= 1); rank in [0, n_d)
+ *   align_elems shard alignment in elements (>= 1; 128 keeps every shard
+ *               start 256-byte aligned for bf16 and 512-byte for fp32)
+ *   out         receives a handle to free with zero_layout_free
+ * Errors: ZERO_EINVAL for a null pointer, n_tensors < 1, a negative size, a
+ * total of 0, n_d < 1, rank outside [0, n_d), align_elems < 1 or an int64
+ * overflow; ZERO_ENOMEM if the host allocation fails. */
+int zero_layout(const int64_t* sizes, int32_t n_tensors, int32_t n_d, int32_t rank,
+                int64_t align_elems, zero_layout_t* out);
+
+/* Copy the layout's facts into *info. ZERO_EINVAL on null arguments. */
+int zero_layout_query(zero_layout_t h, zero_layout_info* info);
+
+/* Copy up to `cap` segments, in shard order, into `segs` (host) and store the
+ * total count in *n_out. segs may be NULL when cap is 0. ZERO_EINVAL on a null
+ * handle or n_out, or cap < 0. */
+int zero_layout_segments(zero_layout_t h, zero_segment* segs, int64_t cap, int64_t* n_out);
+
+/* Release a handle (NULL is ignored). */
+void zero_layout_free(zero_layout_t h);
+
+/* ---------------------------------------------------------------------------
+ * zero_pack_grads -- flatten the rank's gradient slice.
+ * Fills grad_shard[begin, begin+count) (shard coordinates) with the bf16
+ * gradient elements the layout assigns there and writes 0 to padding (notes
+ * on the ZeRO paper, sections 2.2 and 3.2.3: tensors are copied into a
+ * pre-allocated contiguous buffer; section 4.2: the rank keeps its own 1/N_d
+ * gradient slice). A pure bit copy.
+ *   tensor_grads host array of n_tensors DEVICE pointers, entry i = tensor i's
+ *                full gradient (sizes[i] elements, contiguous). Entries of
+ *                tensors with no element in the range may be NULL.
+ *   grad_shard   device pointer to the shard's element 0 (S bf16 values)
+ * Reads only the segments' elements; writes only the range. Source and
+ * destination must not overlap.
+ * Errors: ZERO_EINVAL for a null handle/array/shard, a NULL pointer of a tensor
+ * the range touches, begin < 0, count < 0 or begin+count > S; ZERO_EHIP if a
+ * launch fails. count == 0 enqueues nothing. */
+int zero_pack_grads(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                    int64_t begin, int64_t count, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * zero_shard_sqnorm -- the rank's part of the global gradient norm.
+ * *d_out = sum of g*g over the count bf16 values at d_grad (or *d_out += that
+ * sum when accumulate != 0), each square exact in fp64 and the sum carried in
+ * fp64. The order of additions depends only on count and on the address of
+ * d_grad modulo 16, so equal inputs give bit-identical results. Gradient
+ * clipping must use the norm over all ranks' slices ("ZeRO-3 核心流程",
+ * pitfall 1); callers add the ranks' partial sums (an all-reduce across ranks,
+ * not done here) and hand the per-rank values to zero_adamw_step.
+ *   d_grad      device pointer, count bf16 values
+ *   d_out       device pointer to one double
+ *   d_workspace device scratch of at least zero_sqnorm_workspace_bytes(count)
+ *               bytes, 8-byte aligned; contents on entry do not matter
+ * Errors: ZERO_EINVAL for null pointers (d_grad may be NULL when count == 0),
+ * count < 0 or a workspace that is too small; ZERO_EHIP if a launch fails.
+ * count == 0 writes 0 (or leaves *d_out unchanged when accumulating). */
+size_t zero_sqnorm_workspace_bytes(int64_t count);
+int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int32_t accumulate,
+                      void* d_workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Layout of the fp32 optimizer state (12 bytes per element: master, m, v).
+ * The state of an n-element shard is ONE buffer of 3*n floats in tiles of
+ * ZERO_STATE_TILE elements. Tile k covers elements [k*T, k*T + L_k) with
+ * L_k = min(T, n - k*T) and stores master[L_k], then m[L_k], then v[L_k];
+ * element e (tile k = e / T, j = e % T) has master at 3*k*T + j, m at
+ * 3*k*T + L_k + j and v at 3*k*T + 2*L_k + j. Only the last tile can be
+ * shorter. Keeping the three values of a stretch of elements within one tile
+ * lets the update stream HBM at ~80% of peak on MI355X, where three separate
+ * arrays reach ~70%. zero_state_import/export convert from/to three separate
+ * arrays. */
+#define ZERO_STATE_TILE 8192
+
+/* ---------------------------------------------------------------------------
+ * zero_adamw_step -- fused clip + AdamW + bf16 cast over shard elements
+ * [begin, begin+count).
+ * The rank updates only its own 1/N_d slice of the fp32 master weights and
+ * optimizer state and converts the result to bf16 ("第 5 课：ZeRO 与 FSDP"
+ * section 3; notes on the ZeRO paper, section 4.1), K = 12 bytes of fp32
+ * state per parameter (section 2 of the lesson; notes section 2.1).
+ * Per element, with g the bf16 gradient widened to fp32:
+ *   c  = clip coefficient from G = d_rank_sqnorms[0] + ... + d_rank_sqnorms[n_ranks-1]
+ *        (added in that order in fp64)
+ *   g' = c*g;  m = beta1*m + (1-beta1)*g';  v = beta2*v + (1-beta2)*g'^2
+ *   master = master*(1 - lr*wd) - (lr/(1-beta1^t)) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
+ *   param  = bf16 round-to-nearest-even of the new fp32 master
+ * Arithmetic is fp32 with correctly rounded division and square root.
+ *   d_grad    device pointer to the bf16 gradient shard's element 0
+ *   d_state   device pointer to the tiled fp32 state of all n_state elements
+ *             (layout above); updated in place
+ *   d_param   device pointer to the bf16 parameter shard's element 0; must not
+ *             alias any other buffer
+ *   n_state   elements the state buffer describes (the shard size S)
+ *   begin, count  elements to update; any sub-range of [0, n_state)
+ *   hp        host pointer, read during the call
+ *   d_rank_sqnorms  device array of n_ranks doubles (the ranks' partial sums
+ *             of squares in rank order); may be NULL when max_norm <= 0
+ * Pointers with d_grad/d_param 8-byte and d_state 16-byte alignment take the
+ * vector path, others a slower element path with identical results.
+ * Errors: ZERO_EINVAL for null pointers (all may be NULL when count == 0), a
+ * range outside [0, n_state), step < 1, n_ranks < 1 with clipping on;
+ * ZERO_EHIP if a launch fails. Non-finite inputs propagate per IEEE rules (a
+ * NaN norm gives a NaN coefficient). */
+int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                    int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                    const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream);
+
+/* zero_state_import / zero_state_export -- copy n elements of fp32 master, m
+ * and v between three separate device arrays and the tiled state buffer
+ * (layout above). A bit copy; the arrays must not overlap. For callers whose
+ * optimizer state lives in separate tensors (for example one rank's slice of
+ * a sharded checkpoint, "別再複製本可分片的東西" on sharded checkpoints).
+ * Errors: ZERO_EINVAL for n < 0, NULL or non-4-byte-aligned pointers (NULL is
+ * allowed when n == 0); ZERO_EHIP if a launch fails. */
+int zero_state_import(const float* d_master, const float* d_m, const float* d_v, float* d_state,
+                      int64_t n, hipStream_t stream);
+int zero_state_export(const float* d_state, float* d_master, float* d_m, float* d_v, int64_t n,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * zero_unpack_params -- write the updated bf16 shard back into the tensors.
+ * Copies shard elements [begin, begin+count) of param_shard to the tensor
+ * elements the layout maps them to (the full parameters that the all-gather
+ * reassembles, "第 5 课：ZeRO 与 FSDP" section 3; notes section 4.1; the
+ * updated slice is what the next forward gathers, "ZeRO-3 核心流程" section
+ * 2). Padding goes nowhere; no other tensor byte is written.
+ *   param_shard   device pointer to the shard's element 0
+ *   tensor_params host array of n_tensors DEVICE pointers (NULL allowed for
+ *                 tensors the range does not touch)
+ * Errors as zero_pack_grads. */
+int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* const* tensor_params,
+                       int64_t begin, int64_t count, hipStream_t stream);
+
+/* Message describing the calling thread's last error ("" if none). */
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_MI355X_H */

@@ -1,0 +1,171 @@
+"""The C ABI on the host: the library loads and exports every declared symbol,
+the host partitioner equals the oracle's layout bit for bit, and invalid
+arguments are rejected before anything is enqueued. No call here reaches a
+kernel launch, so these tests need no GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from fsdp_sharded_mixed_zero_amd import synth, zero
+from oracle import memory
+from oracle.layout import LayoutError, build_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(zero.LIB_PATH),
+                                reason="libzero_mi355x.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) == 12, names
+    lib = zero.library()
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding covers the same names
+    for name in names:
+        assert callable(getattr(zero, name)), name
+
+
+def _compare(sizes, n_d, rank, align):
+    ref = build_layout(sizes, n_d, rank, align)
+    lay = zero.zero_layout(sizes, n_d, rank, align)
+    info = lay.info
+    assert info["psi"] == ref.psi
+    assert info["padded"] == ref.padded
+    assert info["shard"] == ref.shard
+    assert info["shard_begin"] == ref.shard_begin
+    assert (info["pad_begin"], info["pad_end"]) == (ref.pad_begin, ref.pad_end)
+    assert info["n_tensors"] == len(sizes) and info["n_d"] == n_d and info["rank"] == rank
+    segs = lay.segments
+    assert segs == [(s.tensor, s.src_off, s.dst_off, s.length) for s in ref.segments]
+    assert info["n_segments"] == len(segs)
+    for stage in range(4):
+        assert info["bytes_stage"][stage] == memory.model_state_bytes_layout(ref.psi, ref.shard, stage)
+        assert info["bytes_stage_fp32acc"][stage] == memory.model_state_bytes_layout(
+            ref.psi, ref.shard, stage, fp32_grad_accum=True)
+        assert info["comm_pages"][stage] == memory.comm_values_pages(ref.psi, stage)
+        assert info["comm_exact"][stage] == memory.comm_values_exact(ref.shard, n_d, stage)
+
+
+def test_layout_matches_oracle_random():
+    rng = np.random.default_rng(99)
+    for _ in range(200):
+        t = int(rng.integers(1, 30))
+        sizes = [int(x) for x in rng.integers(0, 1000, size=t)]
+        if rng.random() < 0.3:
+            sizes[int(rng.integers(0, t))] = 0
+        if sum(sizes) == 0:
+            sizes[0] = 5
+        n_d = int(rng.integers(1, 17))
+        align = int(rng.choice([1, 2, 3, 8, 128]))
+        for rank in {0, n_d - 1, int(rng.integers(0, n_d))}:
+            _compare(sizes, n_d, rank, align)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_layout_matches_oracle_workloads(name):
+    wl = synth.WORKLOADS[name]
+    for rank in sorted({0, wl.rank, wl.n_d - 1}):
+        _compare(list(wl.sizes), wl.n_d, rank, wl.align)
+
+
+def test_layout_rejects_what_the_oracle_rejects():
+    for sizes, n_d, rank, align in [([1, 2], 0, 0, 1), ([1, 2], 2, 2, 1), ([1, 2], 2, -1, 1),
+                                    ([1, -2], 2, 0, 1), ([0, 0], 2, 0, 1), ([4], 2, 0, 0)]:
+        with pytest.raises(LayoutError):
+            build_layout(sizes, n_d, rank, align)
+        with pytest.raises(zero.ZeroError) as err:
+            zero.zero_layout(sizes, n_d, rank, align)
+        assert err.value.code == zero.ZERO_EINVAL
+        assert zero.zero_last_error()
+
+
+def test_layout_rejects_overflow_and_empty_list():
+    with pytest.raises(zero.ZeroError):
+        zero.zero_layout([2**62, 2**62], 1, 0, 1)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_layout([2**61], 1, 0, 1)   # byte report would overflow
+    lib = zero.library()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 1)(5)
+    assert lib.zero_layout(arr, 0, 1, 0, 1, ctypes.byref(h)) == zero.ZERO_EINVAL
+    assert lib.zero_layout(None, 1, 1, 0, 1, ctypes.byref(h)) == zero.ZERO_EINVAL
+    assert lib.zero_layout(arr, 1, 1, 0, 1, None) == zero.ZERO_EINVAL
+
+
+def test_device_calls_reject_bad_arguments_on_the_host():
+    lib = zero.library()
+    lay = zero.zero_layout([100, 28], 2, 1, 8)
+    ptrs = (ctypes.c_void_p * 2)(None, None)
+    # range errors and NULLs are caught before any launch
+    assert lib.zero_pack_grads(lay.handle, ptrs, None, 0, 4, None) == zero.ZERO_EINVAL
+    assert lib.zero_pack_grads(None, ptrs, None, 0, 4, None) == zero.ZERO_EINVAL
+    assert lib.zero_unpack_params(lay.handle, None, ptrs, 0, 4, None) == zero.ZERO_EINVAL
+    assert lib.zero_shard_sqnorm(None, -1, None, 0, None, 0, None) == zero.ZERO_EINVAL
+    assert lib.zero_shard_sqnorm(None, 5, None, 0, None, 0, None) == zero.ZERO_EINVAL
+    hp = zero.hparams(step=0)
+    assert lib.zero_adamw_step(None, None, None, 8, 0, 8, ctypes.byref(hp), None, 1,
+                               None) == zero.ZERO_EINVAL
+    hp = zero.hparams(step=1)
+    for n_state, begin, count in [(8, 0, -1), (8, -1, 2), (8, 4, 5), (-1, 0, 0), (8, 9, 0)]:
+        assert lib.zero_adamw_step(None, None, None, n_state, begin, count, ctypes.byref(hp), None, 1,
+                                   None) == zero.ZERO_EINVAL
+    # clipping on without partial sums
+    assert lib.zero_adamw_step(None, None, None, 8, 0, 8, ctypes.byref(hp), None, 0,
+                               None) == zero.ZERO_EINVAL
+    # NULL buffers with work to do
+    assert lib.zero_adamw_step(None, None, None, 8, 0, 8, ctypes.byref(hp), None, 0,
+                               None) == zero.ZERO_EINVAL
+    assert lib.zero_adamw_step(None, None, None, 8, 0, 8, None, None, 1, None) == zero.ZERO_EINVAL
+    assert "zero_adamw_step" in zero.zero_last_error()
+    assert lib.zero_state_import(None, None, None, None, -1, None) == zero.ZERO_EINVAL
+    assert lib.zero_state_export(None, None, None, None, 5, None) == zero.ZERO_EINVAL
+
+
+def test_state_tile_constant_matches_header():
+    from state_tiles import TILE
+    assert TILE == zero.ZERO_STATE_TILE
+
+
+def test_state_tile_helper_follows_the_stated_layout():
+    # element e of an n-element state: master at 3kT + j, m at 3kT + L + j,
+    # v at 3kT + 2L + j (k = e // T, j = e % T, L = min(T, n - kT))
+    from state_tiles import TILE, from_tiles, to_tiles
+    for n in (1, 5, TILE, TILE + 3, 2 * TILE + 7):
+        master = np.arange(n, dtype=np.float32)
+        st = to_tiles(master, master + 0.25, master + 0.5)
+        for e in {0, n - 1, n // 2, min(n - 1, TILE), min(n - 1, TILE - 1)}:
+            k, j = divmod(e, TILE)
+            L = min(TILE, n - k * TILE)
+            base = 3 * k * TILE
+            assert st[base + j] == e and st[base + L + j] == e + 0.25 and st[base + 2 * L + j] == e + 0.5
+        back = from_tiles(st, n)
+        assert np.array_equal(back[0], master) and np.array_equal(back[2], master + 0.5)
+
+
+def test_workspace_size_is_bounded():
+    sizes = [zero.zero_sqnorm_workspace_bytes(n) for n in (0, 1, 8, 10**6, 10**9, 10**11)]
+    assert all(8 <= s <= 8 * 65536 for s in sizes)
+    assert sizes == sorted(sizes)
+
+
+def test_segments_query_with_small_capacity():
+    lay = zero.zero_layout([10, 10, 10], 1, 0, 1)
+    lib = zero.library()
+    n = ctypes.c_int64()
+    segs = (zero.zero_segment * 1)()
+    assert lib.zero_layout_segments(lay.handle, segs, 1, ctypes.byref(n)) == 0
+    assert n.value == 3 and segs[0].len == 10
+    assert lib.zero_layout_segments(lay.handle, None, 2, ctypes.byref(n)) == zero.ZERO_EINVAL

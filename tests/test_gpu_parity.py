@@ -1,0 +1,385 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, element by
+element, at sizes the oracle finishes in seconds: several tiles plus ragged
+tails, misaligned segments, sub-ranges, empty ranges, many segments, the
+tiny workload end to end for 10 steps."""
+
+import numpy as np
+import pytest
+
+from fsdp_sharded_mixed_zero_amd import synth, zero
+from oracle import step as O
+from oracle.layout import build_layout
+from state_tiles import TILE, from_tiles, to_tiles
+from tolerance import assert_bf16_close, assert_f32_state, assert_norm_close
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def to_dev_u16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def to_host_u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+
+
+def sentinel(n):
+    return torch.full((n,), synth.SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+
+
+def hp_of(ohp, step):
+    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
+                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm,
+                        clip_eps=ohp.clip_eps, step=step)
+
+
+def sqnorm_dev(grad_view, count, accumulate=False, out=None):
+    out = torch.zeros(1, dtype=torch.float64, device=DEV) if out is None else out
+    ws = torch.empty(zero.zero_sqnorm_workspace_bytes(count) // 8, dtype=torch.float64, device=DEV)
+    zero.zero_shard_sqnorm(grad_view, count, out, accumulate, ws)
+    return out
+
+
+# ------------------------------------------------------------- end to end
+
+def test_tiny_workload_ten_steps():
+    """The tiny workload (8 tensors of 131072, N_d = 4, rank 1): all four ranks'
+    shards packed and reduced on the GPU, rank 1 stepped 10 times; every
+    buffer compared with the oracle after every step."""
+    wl = synth.WORKLOADS["tiny"]
+    me = wl.rank
+    ohp = O.AdamWHParams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                         weight_decay=wl.weight_decay, max_norm=wl.max_norm)
+    lays = [build_layout(wl.sizes, wl.n_d, r, wl.align) for r in range(wl.n_d)]
+    handles = [zero.zero_layout(wl.sizes, wl.n_d, r, wl.align) for r in range(wl.n_d)]
+    lay = lays[me]
+    S = lay.shard
+    master0, m0, v0 = synth.host_flat_state(wl, lay.psi, lay.padded)
+    sl = slice(lay.shard_begin, lay.shard_begin + S)
+    o_master, o_m, o_v = master0[sl].copy(), m0[sl].copy(), v0[sl].copy()
+    d_state = to_dev_f32(to_tiles(o_master, o_m, o_v))
+    d_param = torch.empty(S, dtype=torch.bfloat16, device=DEV)
+    d_params = [sentinel(n) for n in wl.sizes]
+    host_params = [np.full(n, synth.SENTINEL, np.uint16) for n in wl.sizes]
+    shards = [torch.empty(l.shard, dtype=torch.bfloat16, device=DEV) for l in lays]
+    partials = torch.zeros(wl.n_d, dtype=torch.float64, device=DEV)
+    hist_m, hist_v = np.abs(o_m), np.abs(o_v)
+    for t in range(1, wl.steps + 1):
+        grads = synth.host_tensor_grads(wl, t)
+        d_grads = [to_dev_u16(g) for g in grads]
+        o_partials = []
+        for r in range(wl.n_d):
+            zero.zero_pack_grads(handles[r], d_grads, shards[r], 0, lays[r].shard)
+            o_shard = O.pack(lays[r], grads)
+            assert np.array_equal(to_host_u16(shards[r]), o_shard), (t, r)
+            zero.zero_shard_sqnorm(shards[r], lays[r].shard, partials[r:r + 1], False,
+                                   torch.empty(64 * 1024, dtype=torch.float64, device=DEV),
+                                   64 * 1024 * 8)
+            o_partials.append(O.sqnorm(o_shard))
+        G = O.global_sqnorm(o_partials)
+        got_partials = partials.cpu().numpy()
+        for r in range(wl.n_d):
+            assert_norm_close(got_partials[r], o_partials[r], f"rank {r} partial")
+        coef = O.clip_coef(G, ohp.max_norm, ohp.clip_eps)
+        assert coef < 1.0     # the tiny workload clips (norm ~ 1.02)
+        zero.zero_adamw_step(shards[me], d_state, d_param, S, 0, S, hp_of(ohp, t), partials, wl.n_d)
+        g_master, g_m, g_v = from_tiles(d_state.cpu().numpy(), S)
+        o_master, o_m, o_v, o_param = O.adamw_step(O.pack(lay, grads), o_master, o_m, o_v, t, ohp, coef)
+        # the GPU's state evolves on its own, so rounding differences of earlier
+        # steps carry forward (decaying): bound m and v by t * 16 ulps of the
+        # largest |value| each element has had on the oracle's trajectory
+        hist_m = np.maximum(hist_m, np.abs(o_m))
+        hist_v = np.maximum(hist_v, np.abs(o_v))
+        assert_f32_state(g_master, o_master, f"master step {t}")
+        assert_f32_state(g_m, o_m, f"m step {t}", hist_m, 16 * t)
+        assert_f32_state(g_v, o_v, f"v step {t}", hist_v, 16 * t)
+        assert_bf16_close(to_host_u16(d_param), o_param, f"param step {t}")
+        zero.zero_unpack_params(handles[me], d_param, d_params, 0, S)
+        host_params = O.unpack(lay, o_param, host_params)
+        for i, (d, h) in enumerate(zip(d_params, host_params)):
+            got = to_host_u16(d)
+            outside = h == synth.SENTINEL
+            assert np.array_equal(got[outside], h[outside]), (t, i)
+            assert_bf16_close(got[~outside], h[~outside], f"tensor {i} step {t}")
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------- pack / unpack
+
+RAGGED = [
+    # (sizes, n_d, align): segments cut at odd element offsets, tails < 8
+    ([3, 100_001, 7, 65_541, 0, 250_000, 13], 3, 1),
+    ([3, 100_001, 7, 65_541, 0, 250_000, 13], 3, 128),
+    ([1_000_003, 5, 77_777], 2, 8),
+    ([8] * 9 + [123_457], 5, 1),
+    ([1], 4, 1),                                     # ranks made of padding only
+]
+
+
+@pytest.mark.parametrize("sizes,n_d,align", RAGGED)
+def test_pack_unpack_ragged(sizes, n_d, align):
+    rng = np.random.default_rng(sum(sizes) + n_d + align)
+    host = [rng.integers(0, 2**16, size=n, dtype=np.uint64).astype(np.uint16) for n in sizes]
+    dev = [to_dev_u16(x) if x.size else torch.empty(0, dtype=torch.bfloat16, device=DEV) for x in host]
+    for rank in range(n_d):
+        lay = build_layout(sizes, n_d, rank, align)
+        h = zero.zero_layout(sizes, n_d, rank, align)
+        S = lay.shard
+        ranges = [(0, S), (0, 0), (S, 0)]
+        for _ in range(4):
+            b = int(rng.integers(0, S + 1))
+            ranges.append((b, int(rng.integers(0, S - b + 1))))
+        for b, c in ranges:
+            # pack writes exactly [b, b+c) of a sentinel-filled shard
+            shard = sentinel(S + 16)[3:3 + S] if rank % 2 else sentinel(S)   # odd offset too
+            zero.zero_pack_grads(h, dev, shard, b, c)
+            got = to_host_u16(shard)
+            want = np.full(S, synth.SENTINEL, np.uint16)
+            want[b:b + c] = O.pack(lay, host, b, c)
+            assert np.array_equal(got, want), (rank, b, c)
+            # unpack of fresh bits into sentinel-filled tensors
+            new = rng.integers(0, 2**16, size=S, dtype=np.uint64).astype(np.uint16)
+            outs = [sentinel(n) for n in sizes]
+            zero.zero_unpack_params(h, to_dev_u16(new), outs, b, c)
+            ref = O.unpack(lay, new[b:b + c], [np.full(n, synth.SENTINEL, np.uint16) for n in sizes], b, c)
+            for i in range(len(sizes)):
+                assert np.array_equal(to_host_u16(outs[i]), ref[i]), (rank, b, c, i)
+
+
+def test_pack_misaligned_tensor_pointers():
+    """Tensor buffers that start at odd element offsets (element path) and
+    segments longer than one block."""
+    rng = np.random.default_rng(4)
+    sizes = [50_000, 70_001, 33]
+    host = [rng.integers(0, 2**16, size=n, dtype=np.uint64).astype(np.uint16) for n in sizes]
+    dev = []
+    for k, x in enumerate(host):
+        buf = sentinel(x.size + 8)
+        view = buf[k + 1:k + 1 + x.size]
+        view.copy_(to_dev_u16(x))
+        dev.append(view)
+    for rank in range(2):
+        lay = build_layout(sizes, 2, rank, 1)
+        h = zero.zero_layout(sizes, 2, rank, 1)
+        shard = sentinel(lay.shard)
+        zero.zero_pack_grads(h, dev, shard, 0, lay.shard)
+        assert np.array_equal(to_host_u16(shard), O.pack(lay, host))
+        outs = []
+        for k, n in enumerate(sizes):
+            outs.append(sentinel(n + 8)[k + 3:k + 3 + n])
+        zero.zero_unpack_params(h, shard, outs, 0, lay.shard)
+        ref = O.unpack(lay, O.pack(lay, host), [np.full(n, synth.SENTINEL, np.uint16) for n in sizes])
+        for o, r in zip(outs, ref):
+            assert np.array_equal(to_host_u16(o), r)
+
+
+def test_pack_more_segments_than_one_launch_holds():
+    sizes = [37] * 150 + [5000]
+    rng = np.random.default_rng(8)
+    host = [rng.integers(0, 2**16, size=n, dtype=np.uint64).astype(np.uint16) for n in sizes]
+    dev = [to_dev_u16(x) for x in host]
+    lay = build_layout(sizes, 1, 0, 128)
+    h = zero.zero_layout(sizes, 1, 0, 128)
+    assert len(lay.segments) > 128
+    shard = sentinel(lay.shard)
+    zero.zero_pack_grads(h, dev, shard, 0, lay.shard)
+    assert np.array_equal(to_host_u16(shard), O.pack(lay, host))
+    outs = [sentinel(n) for n in sizes]
+    zero.zero_unpack_params(h, shard, outs, 0, lay.shard)
+    for o, x in zip(outs, host):
+        assert np.array_equal(to_host_u16(o), x)
+
+
+def test_pack_rejects_missing_tensor_pointer():
+    sizes = [100, 100]
+    h = zero.zero_layout(sizes, 1, 0, 1)
+    shard = sentinel(200)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_pack_grads(h, [to_dev_u16(np.zeros(100, np.uint16)), None], shard, 0, 200)
+    # a range that does not touch the missing tensor is fine
+    zero.zero_pack_grads(h, [to_dev_u16(np.ones(100, np.uint16)), None], shard, 0, 100)
+    assert (to_host_u16(shard)[:100] == 1).all()
+    with pytest.raises(zero.ZeroError):
+        zero.zero_pack_grads(h, [None, None], shard, 150, 60)
+
+
+# --------------------------------------------------------- sum of squares
+
+@pytest.mark.parametrize("count", [0, 1, 7, 8, 9, 1000, 8191, 8192 * 4 + 3, 1 << 20, 5_000_011])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_sqnorm(count, offset):
+    rng = np.random.default_rng(count + offset)
+    bits = synth.to_bf16_bits((rng.standard_normal(count + offset) * 1e-3).astype(np.float32))
+    dev = to_dev_u16(bits)
+    out = sqnorm_dev(dev[offset:], count)
+    got = float(out.cpu()[0])
+    want = O.sqnorm(bits[offset:])
+    if count == 0:
+        assert got == 0.0
+    else:
+        assert_norm_close(got, want)
+        assert abs(got - want) <= 1e-12 * want
+    # bit-identical on a second run; additive in accumulate mode
+    again = float(sqnorm_dev(dev[offset:], count).cpu()[0])
+    assert again == got
+    acc = sqnorm_dev(dev[offset:], count)
+    sqnorm_dev(dev[offset:], count, accumulate=True, out=acc)
+    assert float(acc.cpu()[0]) == 2 * got
+
+
+def test_sqnorm_exact_special_values():
+    ones = to_dev_u16(np.full(1_234_567, 0x3F80, np.uint16))
+    assert float(sqnorm_dev(ones, 1_234_567).cpu()[0]) == 1_234_567.0
+    # squares outside the fp32 range are exact in fp64
+    big = np.array([0x7F7F, 0x0001, 0xC000] * 1000, np.uint16)
+    got = float(sqnorm_dev(to_dev_u16(big), big.size).cpu()[0])
+    assert got == O.sqnorm(big)
+    inf = float(sqnorm_dev(to_dev_u16(np.array([0x3F80, 0x7F80], np.uint16)), 2).cpu()[0])
+    assert np.isinf(inf)
+
+
+def test_sqnorm_rejects_small_workspace():
+    g = to_dev_u16(np.zeros(10_000_000, np.uint16))
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ws = torch.empty(1, dtype=torch.float64, device=DEV)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_shard_sqnorm(g, 10_000_000, out, False, ws)
+
+
+# ------------------------------------------------------------------ AdamW
+
+def _inputs(n, m_std, v_std, seed):
+    rng = np.random.default_rng(seed)
+    bits = synth.to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * m_std).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * v_std).astype(np.float32)
+    return bits, master, m, v
+
+
+def _adamw_case(n, begin, count, step, ohp, n_ranks, m_std, v_std, seed, misalign=False):
+    """Update elements [begin, begin+count) of an n-element shard; with
+    ``misalign`` every base pointer is shifted off its vector alignment."""
+    rng = np.random.default_rng(seed + 1)
+    bits, master, m, v = _inputs(n, m_std, v_std, seed)
+    parts = np.abs(rng.standard_normal(n_ranks)) * 3e-4 * max(n, 1)
+    sh = 1 if misalign else 0
+    d_g = to_dev_u16(np.concatenate([np.zeros(sh, np.uint16), bits]))[sh:]
+    d_s = to_dev_f32(np.concatenate([np.zeros(sh, np.float32), to_tiles(master, m, v)]))[sh:]
+    d_o = sentinel(n + 1)[sh:sh + n]
+    d_parts = torch.from_numpy(parts).to(DEV)
+    zero.zero_adamw_step(d_g, d_s, d_o, n, begin, count, hp_of(ohp, step), d_parts, n_ranks)
+    coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
+    sl = slice(begin, begin + count)
+    want = O.adamw_step(bits[sl], master[sl], m[sl], v[sl], step, ohp, coef)
+    g_master, g_m, g_v = from_tiles(d_s.cpu().numpy(), n)
+    g_o = to_host_u16(d_o)
+    # nothing outside the range moved
+    out = np.ones(n, bool)
+    out[sl] = False
+    assert np.array_equal(g_master[out], master[out])
+    assert np.array_equal(g_m[out], m[out]) and np.array_equal(g_v[out], v[out])
+    assert (g_o[out] == synth.SENTINEL).all()
+    got = (g_master[sl], g_m[sl], g_v[sl], g_o[sl])
+    return got, want, (master[sl], m[sl], v[sl])
+
+
+def _check_adamw(got, want, old):
+    assert_f32_state(got[0], want[0], "master")
+    assert_f32_state(got[1], want[1], "m", old[1])
+    assert_f32_state(got[2], want[2], "v", old[2])
+    assert_bf16_close(got[3], want[3], "param")
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, TILE - 3, TILE + 5, 3 * TILE + 6, 300_001])
+@pytest.mark.parametrize("misalign", [False, True])
+def test_adamw_ragged(n, misalign):
+    ohp = O.AdamWHParams()
+    _check_adamw(*_adamw_case(n, 0, n, 3, ohp, 4, 1e-4, 1e-8, seed=n, misalign=misalign))
+
+
+@pytest.mark.parametrize("begin,count", [(0, 5), (1, 2), (3, 1), (1, 8), (5, TILE), (TILE - 2, 9),
+                                         (4, 3 * TILE), (TILE, 2 * TILE + 5), (7, 0), (2 * TILE + 1, 3)])
+def test_adamw_sub_ranges(begin, count):
+    """Buckets: any [begin, begin+count) of a 3-tile-plus state, tile
+    boundaries and the compact last tile included."""
+    n = 3 * TILE + 10
+    ohp = O.AdamWHParams()
+    _check_adamw(*_adamw_case(n, begin, count, 2, ohp, 2, 1e-4, 1e-8, seed=begin * 7 + count))
+
+
+@pytest.mark.parametrize("step", [1, 2, 1000])
+@pytest.mark.parametrize("n_ranks", [1, 8, 64])
+def test_adamw_steps_and_ranks(step, n_ranks):
+    for ohp in (O.AdamWHParams(), O.AdamWHParams(max_norm=0.0),
+                O.AdamWHParams(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1,
+                               max_norm=1e6)):
+        n = 65_536 + 5
+        _check_adamw(*_adamw_case(n, 0, n, step, ohp, n_ranks, 1e-4, 1e-8, seed=step + n_ranks))
+
+
+def test_adamw_first_step_from_zero_state():
+    # m = v = 0 at step 1: the update is lr * g' / (|g'| + eps) (+ decay)
+    ohp = O.AdamWHParams()
+    _check_adamw(*_adamw_case(100_000, 0, 100_000, 1, ohp, 2, 0.0, 0.0, seed=1))
+
+
+def test_adamw_padding_and_empty():
+    n = 1000
+    s = torch.zeros(3 * n, dtype=torch.float32, device=DEV)
+    g = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    o = sentinel(n)
+    parts = torch.tensor([4.0], dtype=torch.float64, device=DEV)
+    zero.zero_adamw_step(g, s, o, n, 0, n, zero.hparams(step=5), parts, 1)
+    assert not s.any()
+    assert (to_host_u16(o) == 0).all()
+    # count == 0 touches nothing, even with NULL buffers
+    zero.zero_adamw_step(None, None, None, 0, 0, 0, zero.hparams(step=5), parts, 1)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_adamw_step(g, s, o, n, 990, 11, zero.hparams(step=5), parts, 1)
+
+
+def test_adamw_nan_norm_poisons_update():
+    n = 64
+    g = to_dev_u16(np.full(n, 0x3F80, np.uint16))
+    s = to_dev_f32(to_tiles(np.ones(n), np.zeros(n), np.zeros(n)))
+    o = sentinel(n)
+    parts = torch.tensor([float("nan")], dtype=torch.float64, device=DEV)
+    zero.zero_adamw_step(g, s, o, n, 0, n, zero.hparams(step=1), parts, 1)
+    p, m, _ = from_tiles(s.cpu().numpy(), n)
+    assert np.isnan(p).all() and np.isnan(m).all()
+    # an infinite norm gives a zero coefficient: only weight decay moves p
+    s.copy_(to_dev_f32(to_tiles(np.ones(n), np.zeros(n), np.zeros(n))))
+    parts.fill_(float("inf"))
+    zero.zero_adamw_step(g, s, o, n, 0, n, zero.hparams(step=1), parts, 1)
+    p, m, v = from_tiles(s.cpu().numpy(), n)
+    assert (m == 0).all() and (v == 0).all()
+    assert np.allclose(p, 1.0 - 1e-5, rtol=0, atol=1e-7)
+
+
+# -------------------------------------------------------- state layout
+
+@pytest.mark.parametrize("n", [1, 3, 5, TILE, TILE + 1, TILE + 4, 20_003, 3 * TILE])
+@pytest.mark.parametrize("misalign", [False, True])
+def test_state_import_export(n, misalign):
+    rng = np.random.default_rng(n)
+    master, m, v = (rng.standard_normal(n).astype(np.float32) for _ in range(3))
+    sh = 1 if misalign else 0
+
+    def dev(x):
+        return to_dev_f32(np.concatenate([np.zeros(sh, np.float32), x]))[sh:]
+
+    d_state = dev(np.full(3 * n, np.nan, np.float32))
+    zero.zero_state_import(dev(master), dev(m), dev(v), d_state, n)
+    assert np.array_equal(d_state.cpu().numpy(), to_tiles(master, m, v))
+    outs = [dev(np.full(n, np.nan, np.float32)) for _ in range(3)]
+    zero.zero_state_export(d_state, *outs, n)
+    for o, x in zip(outs, (master, m, v)):
+        assert np.array_equal(o.cpu().numpy(), x)
