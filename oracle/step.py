@@ -73,9 +73,9 @@ def pack(layout, tensors, begin: int = 0, count: int | None = None) -> np.ndarra
         hi = min(seg.dst_off + seg.length, end)
         if lo >= hi:
             continue
-        src = np.asarray(tensors[seg.tensor], dtype=np.uint16)
         s0 = seg.src_off + (lo - seg.dst_off)
-        out[lo - begin:hi - begin] = src[s0:s0 + (hi - lo)]
+        out[lo - begin:hi - begin] = np.asarray(tensors[seg.tensor][s0:s0 + (hi - lo)],
+                                                dtype=np.uint16)
     return out
 
 
