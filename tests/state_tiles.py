@@ -39,3 +39,22 @@ def from_tiles(state, n):
         m[lo:lo + L] = state[base + L:base + 2 * L]
         v[lo:lo + L] = state[base + 2 * L:base + 3 * L]
     return master, m, v
+
+
+def tile_span(n, begin, count):
+    """Element span [lo, hi) of the whole tiles that cover [begin, begin+count);
+    the sub-buffer state[3*lo:3*hi] has the same tile structure as an
+    (hi - lo)-element state, because lo is a tile boundary."""
+    lo = (begin // TILE) * TILE
+    hi = min(n, -(-(begin + count) // TILE) * TILE)
+    return lo, hi
+
+
+def state_range(state_slice_fn, n, begin, count):
+    """master, m, v of elements [begin, begin+count) of an n-element tiled
+    state; ``state_slice_fn(a, b)`` returns floats [a, b) of the buffer."""
+    lo, hi = tile_span(n, begin, count)
+    sub = np.asarray(state_slice_fn(3 * lo, 3 * hi), np.float32)
+    master, m, v = from_tiles(sub, hi - lo)
+    sl = slice(begin - lo, begin - lo + count)
+    return master[sl], m[sl], v[sl]

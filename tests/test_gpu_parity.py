@@ -10,7 +10,7 @@ from fsdp_sharded_mixed_zero_amd import synth, zero
 from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import TILE, from_tiles, to_tiles
-from tolerance import assert_bf16_close, assert_f32_state, assert_norm_close
+from tolerance import assert_bf16_close, assert_bf16_param, assert_f32_state, assert_norm_close
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -100,7 +100,7 @@ def test_tiny_workload_ten_steps():
         assert_f32_state(g_master, o_master, f"master step {t}")
         assert_f32_state(g_m, o_m, f"m step {t}", hist_m, 16 * t)
         assert_f32_state(g_v, o_v, f"v step {t}", hist_v, 16 * t)
-        assert_bf16_close(to_host_u16(d_param), o_param, f"param step {t}")
+        assert_bf16_param(to_host_u16(d_param), o_param, o_master, f"param step {t}", g_master)
         zero.zero_unpack_params(handles[me], d_param, d_params, 0, S)
         host_params = O.unpack(lay, o_param, host_params)
         for i, (d, h) in enumerate(zip(d_params, host_params)):
@@ -295,7 +295,7 @@ def _check_adamw(got, want, old):
     assert_f32_state(got[0], want[0], "master")
     assert_f32_state(got[1], want[1], "m", old[1])
     assert_f32_state(got[2], want[2], "v", old[2])
-    assert_bf16_close(got[3], want[3], "param")
+    assert_bf16_param(got[3], want[3], want[0], "param", got[0])
 
 
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, TILE - 3, TILE + 5, 3 * TILE + 6, 300_001])

@@ -1,0 +1,168 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (RankShard.step: whole shard, or 5e7-element buckets for the
+70B shard). The oracle checks sampled ranges element by element; the rank's
+whole-shard sum of squares is recomputed by the oracle over the full shard.
+
+Per workload:
+  * pack: sampled shard ranges equal the oracle's pack of the same ranges of
+    the per-tensor gradients (bit-exact);
+  * sum of squares: the rank's partial equals the oracle's over the whole
+    shard (sqrt within 1e-5, and reported), bit-identical when repeated;
+  * AdamW: sampled ranges of the tiled state and the bf16 shard equal the
+    oracle's update of the same ranges (inputs captured before the step from
+    the input generator, the global norm from the oracle's partial plus the
+    same other-rank inputs);
+  * unpack: the sampled ranges land at the oracle layout's tensor positions,
+    and tensor bytes outside the rank's segments keep their sentinel.
+"""
+
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+from fsdp_sharded_mixed_zero_amd import synth, zero
+from oracle import step as O
+from oracle.layout import build_layout
+from state_tiles import state_range
+from tolerance import assert_bf16_param, assert_f32_state, assert_norm_close
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 1 << 16
+
+
+def u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceTensor:
+    """Slices of a device bf16 tensor fetched on demand, for the oracle's pack."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, sl):
+        return u16(self.t[sl])
+
+
+def sample_ranges(lay, wl, rng):
+    S = lay.shard
+    c = min(SAMPLE, S)
+    starts = {0, S - c}
+    for seg in lay.segments[1:6]:                 # tensor boundaries inside the shard
+        starts.add(min(max(0, seg.dst_off - c // 2), S - c))
+    if wl.bucket:
+        for b in range(wl.bucket, S, wl.bucket * 37):
+            starts.add(min(max(0, b - c // 2 - 3), S - c))    # odd offsets across buckets
+    for _ in range(4):
+        starts.add(int(rng.integers(0, S - c + 1)))
+    return sorted((s, c) for s in starts)
+
+
+def oracle_partial(grad_shard, S):
+    """The oracle's sum of squares of the whole device shard, streamed to the
+    host in pieces (summed in order)."""
+    piece = 1 << 27
+    bounds = [(lo, min(S, lo + piece)) for lo in range(0, S, piece)]
+
+    def one(b):
+        return O.sqnorm(u16(grad_shard[b[0]:b[1]]))
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        parts = list(ex.map(one, bounds))
+    total = 0.0
+    for p in parts:
+        total += p
+    return total
+
+
+@pytest.mark.parametrize("name", ["gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b"])
+def test_workload_full_size(name):
+    from fsdp_sharded_mixed_zero_amd.rank import RankShard
+
+    wl = synth.WORKLOADS[name]
+    lay = build_layout(wl.sizes, wl.n_d, wl.rank, wl.align)
+    S = lay.shard
+    rng = np.random.default_rng(len(wl.sizes))
+    ranges = sample_ranges(lay, wl, rng)
+    print(f"\n[{name}] shard {S}, {len(lay.segments)} segments, bucket {wl.bucket}, "
+          f"{len(ranges)} sampled ranges", flush=True)
+
+    rs = RankShard(wl, fill=False)
+    assert rs.shard == S
+    assert rs.segments == [(s.tensor, s.src_off, s.dst_off, s.length) for s in lay.segments]
+    before = {}
+
+    def capture(lo, hi, master, m, v):
+        for b, c in ranges:
+            a, z = max(b, lo), min(b + c, hi)
+            if a < z:
+                before.setdefault(b, []).append((a, master[a - lo:z - lo].cpu().numpy(),
+                                                 m[a - lo:z - lo].cpu().numpy(),
+                                                 v[a - lo:z - lo].cpu().numpy()))
+
+    rs.fill_state(on_chunk=capture)
+    rs.fill_grads(wl.step)
+    rs.fill_other_ranks()
+    others = rs.rank_sq.cpu().numpy().copy()
+    lazy = [None if t is None else DeviceTensor(t) for t in rs.grads]
+    grads_before = {b: O.pack(lay, lazy, b, c) for b, c in ranges}
+    torch.cuda.synchronize()
+
+    rs.step(wl.step)
+    torch.cuda.synchronize()
+    print(f"[{name}] step done", flush=True)
+
+    # pack: bit-exact on the sampled ranges
+    for b, c in ranges:
+        assert np.array_equal(u16(rs.grad_shard[b:b + c]), grads_before[b]), (name, b)
+
+    # sum of squares over the whole shard
+    got = float(rs.rank_sq[rs.rank].cpu())
+    want = oracle_partial(rs.grad_shard, S)
+    rel = assert_norm_close(got, want, f"{name} partial")
+    print(f"[{name}] partial sum of squares: relative error of sqrt {rel:.2e}", flush=True)
+    again = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for k, (b, n) in enumerate(rs.pieces()):
+        zero.zero_shard_sqnorm(rs.grad_shard[b:], n, again, k > 0, rs.workspace)
+    assert float(again.cpu()) == got                     # bit-identical repeat
+
+    # AdamW on the sampled ranges
+    partials = others.copy()
+    partials[rs.rank] = want
+    coef = O.clip_coef(O.global_sqnorm(partials), wl.max_norm)
+    ohp = O.AdamWHParams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                         weight_decay=wl.weight_decay, max_norm=wl.max_norm)
+    flat_state = rs.state
+    for b, c in ranges:
+        pieces = sorted(before[b], key=lambda x: x[0])
+        master = np.concatenate([p[1] for p in pieces])
+        m = np.concatenate([p[2] for p in pieces])
+        v = np.concatenate([p[3] for p in pieces])
+        assert master.size == c
+        o_master, o_m, o_v, o_param = O.adamw_step(grads_before[b], master, m, v, wl.step, ohp, coef)
+        g_master, g_m, g_v = state_range(lambda a, z: flat_state[a:z].cpu().numpy(), S, b, c)
+        assert_f32_state(g_master, o_master, f"{name} master @{b}")
+        assert_f32_state(g_m, o_m, f"{name} m @{b}", m)
+        assert_f32_state(g_v, o_v, f"{name} v @{b}", v)
+        assert_bf16_param(u16(rs.param_shard[b:b + c]), o_param, o_master, f"{name} param @{b}", g_master)
+        # unpack: the range lands where the oracle layout maps it
+        for seg in lay.segments:
+            lo, hi = max(seg.dst_off, b), min(seg.dst_off + seg.length, b + c)
+            if lo < hi:
+                s0 = seg.src_off + (lo - seg.dst_off)
+                placed = u16(rs.params[seg.tensor][s0:s0 + (hi - lo)])
+                assert np.array_equal(placed, u16(rs.param_shard[lo:hi])), (name, seg.tensor, lo)
+
+    # tensor bytes outside the rank's segments keep the sentinel
+    for seg in (lay.segments[0], lay.segments[-1]):
+        t = rs.params[seg.tensor]
+        inside = seg.length
+        outside = int((t.view(torch.int16) == synth.SENTINEL).sum())
+        assert outside == t.numel() - inside + int(
+            (t.view(torch.int16)[seg.src_off:seg.src_off + seg.length] == synth.SENTINEL).sum())
+    print(f"[{name}] clip coefficient {coef:.6g}; checks passed", flush=True)
+    del rs
+    torch.cuda.empty_cache()
