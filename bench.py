@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-norm", action="store_true",
+                    help="run pack and the sum of squares as two calls instead of the fused one")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into HBM bytes per launch and exit")
@@ -48,6 +50,27 @@ def parse():
 
 
 # ---------------------------------------------------------------- HBM traffic
+
+def kernel_name(raw):
+    """Short kernel name from a profiler's demangled name, template arguments
+    kept (copy_pieces_kernel<true> is pack + sum of squares)."""
+    name = raw.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0].split("::")[-1]
+
+
+def algorithmic_bytes(wl):
+    """Algorithmic HBM bytes per launch of each kernel for the whole shard."""
+    from fsdp_sharded_mixed_zero_amd import zero
+    info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
+    S = info["shard"]
+    real = S - (info["pad_end"] - info["pad_begin"])
+    pad = S - real
+    return S, real, {"copy_pieces_kernel<false>": 4 * real,          # unpack (or unfused pack)
+                     "copy_pieces_kernel<true>": 4 * real + 2 * pad,  # pack + sum of squares
+                     "sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel": 28 * S}
+
 
 def source_hash():
     import hashlib
@@ -73,32 +96,27 @@ def pmc_summary(fetch_dir, write_dir, wl):
         for row in csv.DictReader(open(path)):
             if row["Counter_Name"] != counter:
                 continue
-            name = row["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
-            per.setdefault(name, []).append(float(row["Counter_Value"]))
+            per.setdefault(kernel_name(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
     fetch, n_f = load(fetch_dir, "FETCH_SIZE")
     write, n_w = load(write_dir, "WRITE_SIZE")
-    from fsdp_sharded_mixed_zero_amd import zero
-    info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
-    S = info["shard"]
-    real = S - (info["pad_end"] - info["pad_begin"])
-    copy = next(k for k in fetch if k.endswith("copy_pieces_kernel"))
-    known_read = 2 * real / 1024.0        # KiB per dispatch (pack and unpack alike)
+    S, real, algo = algorithmic_bytes(wl)
+    # the plain copy (unpack) reads and writes exactly 2 bytes per real element
+    copy = "copy_pieces_kernel<false>"
+    known_read = 2 * real / 1024.0        # KiB per dispatch
     known_write = 2 * real / 1024.0
     f_fetch = known_read / fetch[copy]
     f_write = known_write / write[copy]
-    algo = {"copy_pieces_kernel": 4 * real, "sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel": 28 * S}
     kernels = {}
     for k in fetch:
-        short = k.split("::")[-1]
-        if short not in algo and short != "sqnorm_final_kernel":
+        if k not in algo and k != "sqnorm_final_kernel":
             continue
         bytes_ = (fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024.0
-        kernels[short] = {"fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
-                          "dispatches": n_f[k], "traffic_bytes": int(bytes_),
-                          "algorithmic_bytes": algo.get(short),
-                          "traffic_over_algorithmic": round(bytes_ / algo[short], 4) if short in algo else None}
+        kernels[k] = {"fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
+                      "dispatches": n_f[k], "traffic_bytes": int(bytes_),
+                      "algorithmic_bytes": algo.get(k),
+                      "traffic_over_algorithmic": round(bytes_ / algo[k], 4) if k in algo else None}
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
@@ -108,7 +126,7 @@ def pmc_summary(fetch_dir, write_dir, wl):
                 f"python bench.py --workload {wl.name} --pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
             "kernel_source_sha256": source_hash(),
-            "calibration": {"kernel": "copy_pieces_kernel", "known_read_kib": known_read,
+            "calibration": {"kernel": copy, "known_read_kib": known_read,
                             "known_write_kib": known_write, "fetch_factor": round(f_fetch, 5),
                             "write_factor": round(f_write, 5)},
             "kernels": kernels}
@@ -120,12 +138,8 @@ def stats_summary(stats_dir, wl, steps):
     import csv
     import glob
 
-    from fsdp_sharded_mixed_zero_amd import zero
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
-    info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
-    S = info["shard"]
-    real = S - (info["pad_end"] - info["pad_begin"])
-    algo = {"copy_pieces_kernel": 4 * real, "sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel": 28 * S}
+    S, real, algo = algorithmic_bytes(wl)
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} (shard {S} elements)", "",
              "Command (repository root, one MI355X):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o bench -- "
@@ -135,8 +149,7 @@ def stats_summary(stats_dir, wl, steps):
              "| kernel | calls | avg us | min us | max us | algorithmic bytes/launch | GB/s at avg | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|"]
     for row in csv.DictReader(open(path)):
-        name = row["Name"].replace("(anonymous namespace)::", "").split("(")[0]
-        short = name.split("::")[-1]
+        short = kernel_name(row["Name"])
         if short not in algo and short != "sqnorm_final_kernel":
             continue
         avg = float(row["AverageNs"]) / 1e3
@@ -252,7 +265,7 @@ def main():
     zero.library()                       # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
-    rs = RankShard(wl)
+    rs = RankShard(wl, fused_norm=not args.separate_norm)
     torch.cuda.synchronize()
 
     t = wl.step
@@ -261,9 +274,11 @@ def main():
         t += 1
     torch.cuda.synchronize()
     timing = {}
+    per_step = 2 * (len(rs.pieces()) * (2 if args.separate_norm else 1) + 2 * len(rs.pieces()))
+    events = iter([torch.cuda.Event(enable_timing=True) for _ in range(per_step * args.steps)])
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        rs.step(t, timing=timing)
+        rs.step(t, timing=timing, events=events)
         t += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -302,7 +317,7 @@ def main():
                                f"pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack",
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
                    "segments_in_shard": len(rs.segments), "adamw_step": wl.step,
-                   "bucket": rs.bucket},
+                   "bucket": rs.bucket, "norm": "separate" if args.separate_norm else "fused into pack"},
         "adamw_params_per_s": launch_elems / (adamw_launch_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,

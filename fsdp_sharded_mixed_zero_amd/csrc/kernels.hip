@@ -52,6 +52,36 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Sum of squares of the 8 bf16 values in a 16-byte word, each square exact in fp64.
+__device__ __forceinline__ double sq8(u32x4 w, double acc) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double a = double(bf16_lo(w[k]));
+    const double b = double(bf16_hi(w[k]));
+    acc = fma(a, a, acc);
+    acc = fma(b, b, acc);
+  }
+  return acc;
+}
+
+// Fixed-order block sum of one double per thread; result valid in thread 0.
+// Every thread of the block must call it (it synchronises the block).
+template <int THREADS>
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double lds[THREADS / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = x;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) s += lds[w];
+  }
+  return s;
+}
+
 // ============================================================ pack / unpack
 //
 // One launch copies up to kCopyMaxPieces contiguous runs ("pieces"). The
@@ -62,10 +92,13 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 // path. A NULL source writes zeros (padding).
 
 constexpr int kCopyMaxPieces = 64;
-constexpr int kCopyThreads = 256;
+constexpr int kCopyThreads = 256;      // plain copy: one 16-byte vector per lane
+constexpr int kCopySqThreads = 512;    // copy + sum of squares: 2 vectors per lane keep more loads in flight
 constexpr int kCopyVecPerThread = 1;
-constexpr int64_t kCopyVecPerBlock = int64_t(kCopyThreads) * kCopyVecPerThread;  // 256 x 16 B
-constexpr int64_t kCopyElemPerBlock = kCopyVecPerBlock * 8;                       // 2048 bf16
+constexpr int kCopySqVecPerThread = 2;
+constexpr int64_t kCopyVecPerBlock = int64_t(kCopyThreads) * kCopyVecPerThread;
+constexpr int64_t kCopySqVecPerBlock = int64_t(kCopySqThreads) * kCopySqVecPerThread;
+constexpr int64_t kCopySqElemPerBlock = kCopySqVecPerBlock * 8;
 
 struct CopyPieces {
   int32_t n;
@@ -83,17 +116,31 @@ __host__ __device__ inline int64_t copy_head(const void* dst, int64_t len) {
   return h < len ? h : len;
 }
 
-__host__ __device__ inline int64_t copy_blocks(const void* dst, int64_t len, bool vec) {
+// Blocks that a piece of `len` elements at `dst` needs when a block covers
+// per_block 16-byte vectors (or per_block * 8 elements on the element path).
+__host__ __device__ inline int64_t copy_blocks(const void* dst, int64_t len, bool vec, int64_t per_block) {
   if (vec) {
     const int64_t nvec = (len - copy_head(dst, len)) >> 3;
-    const int64_t b = (nvec + kCopyVecPerBlock - 1) / kCopyVecPerBlock;
+    const int64_t b = (nvec + per_block - 1) / per_block;
     return b > 0 ? b : 1;
   }
-  const int64_t b = (len + kCopyElemPerBlock - 1) / kCopyElemPerBlock;
+  const int64_t b = (len + per_block * 8 - 1) / (per_block * 8);
   return b > 0 ? b : 1;
 }
 
-__global__ __launch_bounds__(kCopyThreads) void copy_pieces_kernel(const CopyPieces P) {
+__device__ __forceinline__ double sq1(uint16_t h, double acc) {
+  const double x = double(__uint_as_float(uint32_t(h) << 16));
+  return fma(x, x, acc);
+}
+
+// SQ: also sum the squares of the values copied (fp64) and write one partial
+// per block to partial[blockIdx.x].
+template <bool SQ>
+__global__ __launch_bounds__(SQ ? kCopySqThreads : kCopyThreads) void copy_pieces_kernel(
+    const CopyPieces P, double* __restrict__ partial) {
+  constexpr int THREADS = SQ ? kCopySqThreads : kCopyThreads;
+  constexpr int VPT = SQ ? kCopySqVecPerThread : kCopyVecPerThread;
+  constexpr int64_t VEC_PER_BLOCK = int64_t(THREADS) * VPT;
   const int64_t b = blockIdx.x;
   // the piece this block serves: the last p with first_block[p] <= b
   int lo = 0, hi = P.n - 1;
@@ -107,38 +154,56 @@ __global__ __launch_bounds__(kCopyThreads) void copy_pieces_kernel(const CopyPie
   uint16_t* __restrict__ dst = P.dst[p];
   const int64_t len = P.len[p];
   const int t = threadIdx.x;
+  double acc = 0.0;
 
   if ((P.vec_mask >> p) & 1u) {
     const int64_t head = copy_head(dst, len);
     const int64_t nvec = (len - head) >> 3;
     const int64_t tail0 = head + nvec * 8;
     if (lb == 0) {
-      if (t < head) dst[t] = src ? src[t] : uint16_t(0);
+      if (t < head) {
+        const uint16_t x = src ? src[t] : uint16_t(0);
+        dst[t] = x;
+        if (SQ) acc = sq1(x, acc);
+      }
       const int64_t k = tail0 + (t - 8);
-      if (t >= 8 && k < len) dst[k] = src ? src[k] : uint16_t(0);
+      if (t >= 8 && k < len) {
+        const uint16_t x = src ? src[k] : uint16_t(0);
+        dst[k] = x;
+        if (SQ) acc = sq1(x, acc);
+      }
     }
     const u32x4* __restrict__ s = reinterpret_cast<const u32x4*>(src + head);
     u32x4* __restrict__ d = reinterpret_cast<u32x4*>(dst + head);
-    const int64_t base = lb * kCopyVecPerBlock + t;
-    u32x4 r[kCopyVecPerThread];
+    const int64_t base = lb * VEC_PER_BLOCK + t;
+    u32x4 r[VPT];
 #pragma unroll
-    for (int k = 0; k < kCopyVecPerThread; ++k) {
-      const int64_t i = base + int64_t(k) * kCopyThreads;
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t i = base + int64_t(k) * THREADS;
       r[k] = (src && i < nvec) ? __builtin_nontemporal_load(s + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int k = 0; k < kCopyVecPerThread; ++k) {
-      const int64_t i = base + int64_t(k) * kCopyThreads;
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t i = base + int64_t(k) * THREADS;
       if (i < nvec) __builtin_nontemporal_store(r[k], d + i);
+      if (SQ) acc = sq8(r[k], acc);   // zero vectors past the end add nothing
     }
   } else {
-    const int64_t base = lb * kCopyElemPerBlock + t;
-    constexpr int kPer = int(kCopyElemPerBlock / kCopyThreads);
+    const int64_t base = lb * VEC_PER_BLOCK * 8 + t;
+    constexpr int kPer = VPT * 8;
 #pragma unroll 8
     for (int k = 0; k < kPer; ++k) {
-      const int64_t i = base + int64_t(k) * kCopyThreads;
-      if (i < len) dst[i] = src ? src[i] : uint16_t(0);
+      const int64_t i = base + int64_t(k) * THREADS;
+      if (i < len) {
+        const uint16_t x = src ? src[i] : uint16_t(0);
+        dst[i] = x;
+        if (SQ) acc = sq1(x, acc);
+      }
     }
+  }
+  if (SQ) {
+    const double s = block_sum<THREADS>(acc);
+    if (t == 0) partial[blockIdx.x] = s;
   }
 }
 
@@ -153,8 +218,14 @@ constexpr int64_t kCopyMaxBlocksPerLaunch = int64_t(1) << 23;
 // Pieces are cut to at most 2^34 elements (2^21 blocks) so any piece fits.
 constexpr int64_t kCopyMaxPieceElems = int64_t(1) << 34;
 
-int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who) {
+// Launches copying `pieces`, batched by kCopyMaxPieces and by the block limit.
+// With `partial` non-NULL the sum-of-squares variant runs and each block writes
+// partial[k] (k counts blocks across all launches); *n_partial gets the count.
+int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who,
+                  double* partial = nullptr, int64_t* n_partial = nullptr) {
+  const int64_t per_block = partial ? kCopySqVecPerBlock : kCopyVecPerBlock;
   size_t i = 0;
+  int64_t done = 0;
   while (i < pieces.size()) {
     CopyPieces P{};
     int64_t blocks = 0;
@@ -163,7 +234,7 @@ int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const ch
       const Piece& pc = pieces[i];
       const bool vec = pc.src == nullptr ||
                        ((uintptr_t(pc.src) & 15u) == (uintptr_t(pc.dst) & 15u));
-      const int64_t nb = copy_blocks(pc.dst, pc.len, vec);
+      const int64_t nb = copy_blocks(pc.dst, pc.len, vec, per_block);
       if (n > 0 && blocks + nb > kCopyMaxBlocksPerLaunch) break;  // launch what we have first
       P.src[n] = pc.src;
       P.dst[n] = pc.dst;
@@ -175,11 +246,26 @@ int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const ch
     P.n = n;
     P.first_block[n] = blocks;
     if (blocks > kCopyMaxBlocksPerLaunch) return fail(ZERO_EINVAL, "%s: piece too large for one launch", who);
-    hipLaunchKernelGGL(copy_pieces_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, stream, P);
+    if (partial)
+      hipLaunchKernelGGL(copy_pieces_kernel<true>, dim3(unsigned(blocks)), dim3(kCopySqThreads), 0, stream, P,
+                         partial + done);
+    else
+      hipLaunchKernelGGL(copy_pieces_kernel<false>, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, stream, P,
+                         nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    done += blocks;
   }
+  if (n_partial) *n_partial = done;
   return zero::ok();
+}
+
+// Upper bound of the blocks the sum-of-squares copy uses for pieces of these
+// lengths: ceil(len / elements per block) + 1 each, whatever the alignment.
+int64_t pieces_block_bound(const std::vector<int64_t>& lens) {
+  int64_t b = 0;
+  for (int64_t len : lens) b += (len + kCopySqElemPerBlock - 1) / kCopySqElemPerBlock + 1;
+  return b;
 }
 
 // Pieces of shard range [begin, begin+count): one per segment overlap, plus
@@ -250,34 +336,6 @@ int sq_blocks(int64_t count) {
   return int(b);
 }
 
-__device__ __forceinline__ double sq8(u32x4 w, double acc) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const double a = double(bf16_lo(w[k]));
-    const double b = double(bf16_hi(w[k]));
-    acc = fma(a, a, acc);
-    acc = fma(b, b, acc);
-  }
-  return acc;
-}
-
-// Fixed-order block sum of one double per thread; result valid in thread 0.
-template <int THREADS>
-__device__ __forceinline__ double block_sum(double x) {
-  __shared__ double lds[THREADS / 64];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) lds[wave] = x;
-  __syncthreads();
-  double s = 0.0;
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 0; w < THREADS / 64; ++w) s += lds[w];
-  }
-  return s;
-}
-
 __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(const uint16_t* __restrict__ g,
                                                                      int64_t count, int64_t head,
                                                                      double* __restrict__ partial) {
@@ -313,11 +371,19 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(const uint16
 }
 
 __global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const double* __restrict__ partial,
-                                                                        int n, double* __restrict__ out,
+                                                                        int64_t n, double* __restrict__ out,
                                                                         int accumulate) {
-  double acc = 0.0;
-  for (int i = threadIdx.x; i < n; i += kSqFinalThreads) acc += partial[i];
-  const double s = block_sum<kSqFinalThreads>(acc);
+  constexpr int T = kSqFinalThreads;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * T < n; i += 4 * T) {   // four independent loads in flight per lane
+    a0 += partial[i];
+    a1 += partial[i + T];
+    a2 += partial[i + 2 * T];
+    a3 += partial[i + 3 * T];
+  }
+  for (; i < n; i += T) a0 += partial[i];
+  const double s = block_sum<kSqFinalThreads>((a0 + a1) + (a2 + a3));
   if (threadIdx.x == 0) *out = accumulate ? *out + s : s;
 }
 
@@ -511,6 +577,52 @@ extern "C" int zero_pack_grads(zero_layout_t h, const uint16_t* const* tensor_gr
                             &pieces, who))
     return rc;
   return launch_pieces(pieces, stream, who);
+}
+
+// Lengths of the pieces pack would copy for shard range [begin, begin+count).
+static std::vector<int64_t> pack_piece_lengths(const zero_layout_s* h, int64_t begin, int64_t count) {
+  std::vector<int64_t> lens;
+  const int64_t end = begin + count;
+  for (const zero_segment& g : h->segs) {
+    const int64_t lo = std::max(g.dst_off, begin), hi = std::min(g.dst_off + g.len, end);
+    for (int64_t a = lo; a < hi; a += kCopyMaxPieceElems) lens.push_back(std::min(kCopyMaxPieceElems, hi - a));
+  }
+  const int64_t lo = std::max(h->info.pad_begin, begin), hi = std::min(h->info.pad_end, end);
+  for (int64_t a = lo; a < hi; a += kCopyMaxPieceElems) lens.push_back(std::min(kCopyMaxPieceElems, hi - a));
+  return lens;
+}
+
+extern "C" size_t zero_pack_sqnorm_workspace_bytes(zero_layout_t h, int64_t begin, int64_t count) {
+  if (h == nullptr || check_range(h, begin, count, "zero_pack_sqnorm_workspace_bytes") != ZERO_OK) return 0;
+  const int64_t blocks = pieces_block_bound(pack_piece_lengths(h, begin, count));
+  return size_t(std::max<int64_t>(blocks, 1)) * sizeof(double);
+}
+
+extern "C" int zero_pack_grads_sqnorm(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                                      int64_t begin, int64_t count, double* d_out, int32_t accumulate,
+                                      void* d_workspace, size_t ws_bytes, hipStream_t stream) {
+  static const char* who = "zero_pack_grads_sqnorm";
+  if (h == nullptr || tensor_grads == nullptr || grad_shard == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL handle, tensor array or shard", who);
+  if (d_out == nullptr || d_workspace == nullptr) return fail(ZERO_EINVAL, "%s: NULL output or workspace", who);
+  if (int rc = check_range(h, begin, count, who)) return rc;
+  if (uintptr_t(grad_shard) & 1u) return fail(ZERO_EINVAL, "%s: shard pointer is not 2-byte aligned", who);
+  if (uintptr_t(d_workspace) & 7u) return fail(ZERO_EINVAL, "%s: workspace is not 8-byte aligned", who);
+  const int64_t bound = std::max<int64_t>(pieces_block_bound(pack_piece_lengths(h, begin, count)), 1);
+  if (ws_bytes < size_t(bound) * sizeof(double))
+    return fail(ZERO_EINVAL, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, size_t(bound) * sizeof(double));
+  std::vector<Piece> pieces;
+  if (int rc = build_pieces(h, const_cast<uint16_t* const*>(tensor_grads), grad_shard, begin, count, true,
+                            &pieces, who))
+    return rc;
+  double* part = static_cast<double*>(d_workspace);
+  int64_t n_part = 0;
+  if (int rc = launch_pieces(pieces, stream, who, part, &n_part)) return rc;
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, part, n_part, d_out,
+                     accumulate ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
 }
 
 extern "C" int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* const* tensor_params,

@@ -27,7 +27,7 @@ from . import synth, zero
 
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
-                 fill: bool = True, bucket: int | None = None):
+                 fill: bool = True, bucket: int | None = None, fused_norm: bool = True):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -47,12 +47,15 @@ class RankShard:
             self.grads[i] = torch.empty(wl.sizes[i], dtype=torch.bfloat16, device=dev)
             self.params[i] = torch.full((wl.sizes[i],), synth.SENTINEL, dtype=torch.int16,
                                         device=dev).view(torch.bfloat16)
+        self.grad_ptrs = zero.pointer_array(self.grads)
+        self.param_ptrs = zero.pointer_array(self.params)
         self.grad_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
         self.param_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
         self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
-        piece = self.bucket if self.bucket > 0 else S
-        ws = zero.zero_sqnorm_workspace_bytes(piece)
+        self.fused_norm = fused_norm
+        ws = max(max(zero.zero_sqnorm_workspace_bytes(n),
+                     zero.zero_pack_sqnorm_workspace_bytes(self.layout, b, n)) for b, n in self.pieces())
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=dev)
         if fill:
             self.fill_state()
@@ -115,27 +118,36 @@ class RankShard:
             return [(0, self.shard)]
         return [(b, min(self.bucket, self.shard - b)) for b in range(0, self.shard, self.bucket)]
 
-    def step(self, step, stream=None, timing=None):
-        """One local step. ``timing``: optional dict; each phase ("pack",
-        "sqnorm", "adamw", "unpack") gets a list of (start, end) CUDA events
-        recorded around its launches on the current stream."""
+    def step(self, step, stream=None, timing=None, events=None):
+        """One local step. ``timing``: optional dict; each phase ("pack_sqnorm"
+        or "pack" and "sqnorm", "adamw", "unpack") gets a list of (start, end)
+        CUDA events recorded around its launches on the current stream, taken
+        from the iterator ``events`` (pre-created, so timing adds no event
+        creation to the step)."""
         hp = self.hparams(step)
         own = self.rank_sq[self.rank:self.rank + 1]
         pieces = self.pieces()
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
 
         def mark(phase, fn):
             if timing is None:
                 fn()
                 return
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
+            e1 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
             e1.record()
             timing.setdefault(phase, []).append((e0, e1))
 
         for k, (b, n) in enumerate(pieces):
-            mark("pack", lambda: zero.zero_pack_grads(self.layout, self.grads, self.grad_shard, b, n,
+            if self.fused_norm:
+                mark("pack_sqnorm", lambda: zero.zero_pack_grads_sqnorm(
+                    self.layout, self.grad_ptrs, self.grad_shard, b, n, own, k > 0, self.workspace,
+                    stream=stream))
+                continue
+            mark("pack", lambda: zero.zero_pack_grads(self.layout, self.grad_ptrs, self.grad_shard, b, n,
                                                       stream))
             mark("sqnorm", lambda: zero.zero_shard_sqnorm(self.grad_shard[b:], n, own, k > 0,
                                                           self.workspace, stream=stream))
@@ -143,13 +155,18 @@ class RankShard:
             mark("adamw", lambda: zero.zero_adamw_step(
                 self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
                 self.wl.n_d, stream))
-            mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.params,
+            mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
 
     def bytes_per_step(self):
-        """Algorithmic HBM bytes of one step: pack 4, sum of squares 2, AdamW 28
-        and unpack 4 bytes per shard element (pack writes only 2 on padding,
-        unpack moves nothing there)."""
+        """Algorithmic HBM bytes of one step: pack 4, sum of squares 2 (0 when
+        fused into pack), AdamW 28 and unpack 4 bytes per shard element (pack
+        writes only 2 on padding, unpack moves nothing there)."""
         pad = self.shard - self.real
-        return {"pack": 4 * self.real + 2 * pad, "sqnorm": 2 * self.shard,
-                "adamw": 28 * self.shard, "unpack": 4 * self.real}
+        pack = 4 * self.real + 2 * pad
+        out = {"adamw": 28 * self.shard, "unpack": 4 * self.real}
+        if self.fused_norm:
+            out["pack_sqnorm"] = pack
+        else:
+            out.update(pack=pack, sqnorm=2 * self.shard)
+        return out

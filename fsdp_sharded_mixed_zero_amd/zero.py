@@ -72,6 +72,9 @@ _SIGNATURES = {
     "zero_layout_free": (None, [_VP]),
     "zero_pack_grads": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP]),
     "zero_sqnorm_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "zero_pack_sqnorm_workspace_bytes": (ctypes.c_size_t, [_VP, _I64, _I64]),
+    "zero_pack_grads_sqnorm": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP, _I32, _VP,
+                                              ctypes.c_size_t, _VP]),
     "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                        ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
@@ -127,10 +130,18 @@ def _stream(stream):
 
 
 def _ptr_array(items):
+    if isinstance(items, ctypes.Array):
+        return items
     arr = (_VP * len(items))()
     for i, t in enumerate(items):
         arr[i] = _ptr(t)
     return arr
+
+
+def pointer_array(tensors):
+    """A reusable host array of device pointers (tensor_grads/tensor_params
+    arguments); None entries stay NULL."""
+    return _ptr_array(tensors)
 
 
 class Layout:
@@ -191,6 +202,20 @@ def zero_pack_grads(layout: Layout, tensor_grads, grad_shard, begin: int, count:
     arr = _ptr_array(tensor_grads)
     _check("zero_pack_grads", library().zero_pack_grads(
         layout.handle, arr, _ptr(grad_shard), begin, count, _stream(stream)))
+
+
+def zero_pack_sqnorm_workspace_bytes(layout: Layout, begin: int, count: int) -> int:
+    return int(library().zero_pack_sqnorm_workspace_bytes(layout.handle, begin, count))
+
+
+def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, out,
+                           accumulate: bool, workspace, ws_bytes: int | None = None, stream=None):
+    arr = _ptr_array(tensor_grads)
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_pack_grads_sqnorm", library().zero_pack_grads_sqnorm(
+        layout.handle, arr, _ptr(grad_shard), begin, count, _ptr(out), 1 if accumulate else 0,
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def zero_unpack_params(layout: Layout, param_shard, tensor_params, begin: int, count: int, stream=None):

@@ -151,6 +151,30 @@ int zero_pack_grads(zero_layout_t h, const uint16_t* const* tensor_grads, uint16
                     int64_t begin, int64_t count, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * zero_pack_grads_sqnorm -- zero_pack_grads and the sum of squares of the
+ * packed range in one pass: the gradient norm is taken over the values as
+ * they are flattened into the fused buffer (notes on the ZeRO paper, sections
+ * 2.2 and 5.2: flattening feeds the gradient-norm computation), so the shard
+ * is not read a second time. Writes grad_shard[begin, begin+count) exactly as
+ * zero_pack_grads does, and *d_out = sum of g*g over that range (or
+ * *d_out += it when accumulate != 0), each square exact in fp64, summed in
+ * fp64 in an order fixed by the layout, the range and the pointers' alignment
+ * (equal inputs give bit-identical results; the order differs from
+ * zero_shard_sqnorm's, so the two may differ in the last bits).
+ *   d_out        device pointer to one double
+ *   d_workspace  device scratch of at least zero_pack_sqnorm_workspace_bytes(h,
+ *                begin, count) bytes, 8-byte aligned; contents on entry do not
+ *                matter
+ * Errors: as zero_pack_grads, plus ZERO_EINVAL for a NULL output or workspace,
+ * or a workspace that is too small. count == 0 writes 0 (or leaves *d_out
+ * unchanged when accumulating). zero_pack_sqnorm_workspace_bytes returns 0
+ * for a NULL handle or a range outside the shard. */
+size_t zero_pack_sqnorm_workspace_bytes(zero_layout_t h, int64_t begin, int64_t count);
+int zero_pack_grads_sqnorm(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                           int64_t begin, int64_t count, double* d_out, int32_t accumulate,
+                           void* d_workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * zero_shard_sqnorm -- the rank's part of the global gradient norm.
  * *d_out = sum of g*g over the count bf16 values at d_grad (or *d_out += that
  * sum when accumulate != 0), each square exact in fp64 and the sum carried in

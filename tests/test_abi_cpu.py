@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = zero.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -131,6 +131,10 @@ def test_device_calls_reject_bad_arguments_on_the_host():
     assert lib.zero_adamw_step(None, None, None, 8, 0, 8, None, None, 1, None) == zero.ZERO_EINVAL
     assert "zero_adamw_step" in zero.zero_last_error()
     assert lib.zero_state_import(None, None, None, None, -1, None) == zero.ZERO_EINVAL
+    assert lib.zero_pack_grads_sqnorm(lay.handle, ptrs, None, 0, 4, None, 0, None, 0, None) == zero.ZERO_EINVAL
+    assert lib.zero_pack_sqnorm_workspace_bytes(None, 0, 4) == 0
+    assert lib.zero_pack_sqnorm_workspace_bytes(lay.handle, 0, 10**6) == 0     # range outside
+    assert lib.zero_pack_sqnorm_workspace_bytes(lay.handle, 0, 64) >= 8
     assert lib.zero_state_export(None, None, None, None, 5, None) == zero.ZERO_EINVAL
 
 

@@ -153,6 +153,43 @@ def test_pack_unpack_ragged(sizes, n_d, align):
                 assert np.array_equal(to_host_u16(outs[i]), ref[i]), (rank, b, c, i)
 
 
+@pytest.mark.parametrize("sizes,n_d,align", RAGGED)
+def test_pack_with_sum_of_squares(sizes, n_d, align):
+    """The fused pack: the same bytes as the oracle's pack and the oracle's
+    sum of squares of the packed range; bit-identical when repeated."""
+    rng = np.random.default_rng(sum(sizes) * 3 + n_d)
+    host = [synth.to_bf16_bits((rng.standard_normal(n) * 1e-2).astype(np.float32)) for n in sizes]
+    dev = [to_dev_u16(x) if x.size else torch.empty(0, dtype=torch.bfloat16, device=DEV) for x in host]
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for rank in range(n_d):
+        lay = build_layout(sizes, n_d, rank, align)
+        h = zero.zero_layout(sizes, n_d, rank, align)
+        S = lay.shard
+        ranges = [(0, S), (0, 0)]
+        for _ in range(3):
+            b = int(rng.integers(0, S + 1))
+            ranges.append((b, int(rng.integers(0, S - b + 1))))
+        for b, c in ranges:
+            ws_bytes = zero.zero_pack_sqnorm_workspace_bytes(h, b, c)
+            ws = torch.empty(ws_bytes // 8, dtype=torch.float64, device=DEV)
+            shard = sentinel(S + 16)[5:5 + S] if rank % 2 else sentinel(S)
+            zero.zero_pack_grads_sqnorm(h, dev, shard, b, c, out, False, ws)
+            want_bits = O.pack(lay, host, b, c)
+            got = to_host_u16(shard)
+            assert np.array_equal(got[b:b + c], want_bits), (rank, b, c)
+            assert (got[:b] == synth.SENTINEL).all() and (got[b + c:] == synth.SENTINEL).all()
+            total = float(out.cpu()[0])
+            want = O.sqnorm(want_bits)
+            assert abs(total - want) <= 1e-12 * want, (rank, b, c, total, want)
+            zero.zero_pack_grads_sqnorm(h, dev, shard, b, c, out, True, ws)
+            assert float(out.cpu()[0]) == 2 * total
+            zero.zero_pack_grads_sqnorm(h, dev, shard, b, c, out, False, ws)
+            assert float(out.cpu()[0]) == total
+            if ws_bytes > 8:
+                with pytest.raises(zero.ZeroError):
+                    zero.zero_pack_grads_sqnorm(h, dev, shard, b, c, out, False, ws, ws_bytes - 8)
+
+
 def test_pack_misaligned_tensor_pointers():
     """Tensor buffers that start at odd element offsets (element path) and
     segments longer than one block."""

@@ -78,8 +78,9 @@ def oracle_partial(grad_shard, S):
     return total
 
 
+@pytest.mark.parametrize("fused_norm", [True, False], ids=["fused-norm", "separate-norm"])
 @pytest.mark.parametrize("name", ["gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b"])
-def test_workload_full_size(name):
+def test_workload_full_size(name, fused_norm):
     from fsdp_sharded_mixed_zero_amd.rank import RankShard
 
     wl = synth.WORKLOADS[name]
@@ -88,9 +89,9 @@ def test_workload_full_size(name):
     rng = np.random.default_rng(len(wl.sizes))
     ranges = sample_ranges(lay, wl, rng)
     print(f"\n[{name}] shard {S}, {len(lay.segments)} segments, bucket {wl.bucket}, "
-          f"{len(ranges)} sampled ranges", flush=True)
+          f"{len(ranges)} sampled ranges, fused norm {fused_norm}", flush=True)
 
-    rs = RankShard(wl, fill=False)
+    rs = RankShard(wl, fill=False, fused_norm=fused_norm)
     assert rs.shard == S
     assert rs.segments == [(s.tensor, s.src_off, s.dst_off, s.length) for s in lay.segments]
     before = {}
@@ -126,7 +127,11 @@ def test_workload_full_size(name):
     print(f"[{name}] partial sum of squares: relative error of sqrt {rel:.2e}", flush=True)
     again = torch.zeros(1, dtype=torch.float64, device="cuda")
     for k, (b, n) in enumerate(rs.pieces()):
-        zero.zero_shard_sqnorm(rs.grad_shard[b:], n, again, k > 0, rs.workspace)
+        if fused_norm:
+            zero.zero_pack_grads_sqnorm(rs.layout, rs.grads, rs.grad_shard, b, n, again, k > 0,
+                                        rs.workspace)
+        else:
+            zero.zero_shard_sqnorm(rs.grad_shard[b:], n, again, k > 0, rs.workspace)
     assert float(again.cpu()) == got                     # bit-identical repeat
 
     # AdamW on the sampled ranges
