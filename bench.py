@@ -132,32 +132,42 @@ def pmc_summary(fetch_dir, write_dir, wl):
             "kernels": kernels}
 
 
-def stats_summary(stats_dir, wl, steps):
-    """Markdown table of a rocprofv3 kernel-stats CSV with achieved bandwidth
-    from each kernel's algorithmic bytes per launch."""
+def stats_summary(stats_dir, wl, steps, warmup):
+    """Markdown table of a rocprofv3 kernel-stats CSV of this benchmark, with
+    achieved bandwidth from each kernel's algorithmic bytes per launch (the
+    step's bytes spread over that kernel's launches per step)."""
     import csv
     import glob
 
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     S, real, algo = algorithmic_bytes(wl)
-    lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} (shard {S} elements)", "",
+    rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
+    pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
+    steps_run = int(rows["adamw_vec_kernel"]["Calls"]) / pieces      # warm-up steps included
+    lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
+             f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
              "Command (repository root, one MI355X):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o bench -- "
-             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup 10 --no-cpu-baseline",
-             f"    python bench.py --workload {wl.name} --stats-summary {stats_dir}", "",
+             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup} --no-cpu-baseline",
+             f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup} "
+             f"--stats-summary {stats_dir}", "",
              f"kernels.hip sha256: `{source_hash()}`", "",
-             "| kernel | calls | avg us | min us | max us | algorithmic bytes/launch | GB/s at avg | % of 8 TB/s |",
-             "|---|---|---|---|---|---|---|---|"]
-    for row in csv.DictReader(open(path)):
-        short = kernel_name(row["Name"])
+             f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "
+             f"kernel divided by its launches per step.", "",
+             "| kernel | calls | launches/step | avg us | min us | max us | algorithmic bytes/launch | "
+             "GB/s at avg | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for short, row in rows.items():
         if short not in algo and short != "sqnorm_final_kernel":
             continue
+        calls = int(row["Calls"])
+        per_step = calls / steps_run
         avg = float(row["AverageNs"]) / 1e3
-        b = algo.get(short)
+        b = algo[short] / per_step if short in algo else None
         gbps = f"{b / (avg * 1e-6) / 1e9:.1f}" if b else "-"
         pct = f"{100 * b / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}" if b else "-"
-        lines.append(f"| {short} | {row['Calls']} | {avg:.1f} | {float(row['MinNs']) / 1e3:.1f} | "
-                     f"{float(row['MaxNs']) / 1e3:.1f} | {b if b else '-'} | {gbps} | {pct} |")
+        lines.append(f"| {short} | {calls} | {per_step:.2f} | {avg:.1f} | {float(row['MinNs']) / 1e3:.1f} | "
+                     f"{float(row['MaxNs']) / 1e3:.1f} | {int(b) if b else '-'} | {gbps} | {pct} |")
     return "\n".join(lines) + "\n"
 
 
@@ -248,7 +258,8 @@ def main():
         return
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth
-        print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps), end="")
+        print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup),
+              end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
