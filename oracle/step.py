@@ -130,6 +130,33 @@ def clip_coef(global_sq: float, max_norm: float, clip_eps: float = 1e-6) -> floa
     return 1.0 if ratio >= 1.0 else ratio
 
 
+# ------------------------------------------------ fp32 gradient accumulation
+#
+# "第 5 课：ZeRO 与 FSDP", section 2 (note on fp32 gradient accumulation):
+# with ZeRO-2/3 each rank keeps an fp32 accumulator for its own gradient slice
+# (4 Psi / N_d extra bytes); every micro-batch's 16-bit gradient slice is added
+# into it, and the optimizer step then reads fp32 gradients.
+
+def accumulate(acc, grad_bits, first: bool):
+    """acc + g for one micro-batch, stored as fp32 (round to nearest even);
+    ``first`` starts from zero. The fp64 sum is exact whenever the fp32 result
+    can differ from acc, so rounding it once to fp32 is the correctly rounded
+    fp32 sum."""
+    g = bf16_to_f32(grad_bits).astype(np.float64)
+    base = 0.0 if first else np.asarray(acc, dtype=np.float32).astype(np.float64)
+    return (base + g).astype(np.float32)
+
+
+def sqnorm_f32(grad):
+    """Sum of squares of an fp32 gradient range in fp64 (each square exact)."""
+    x = np.asarray(grad, dtype=np.float32).reshape(-1)
+    total = 0.0
+    for lo in range(0, x.size, CHUNK):
+        y = x[lo:lo + CHUNK].astype(np.float64)
+        total += float(np.dot(y, y))
+    return total
+
+
 # ---------------------------------------------------------------------- AdamW
 
 def adamw_f64(p, m, v, g_hat, step: int, hp: AdamWHParams):
@@ -154,11 +181,17 @@ def adamw_step(grad_bits, master, m, v, step: int, hp: AdamWHParams, coef: float
     """The rank's fused update over its shard range: scale the bf16 gradient by
     the clip coefficient, update master/m/v (stored back as fp32) and produce
     the bf16 parameter shard. Returns (master', m', v', param_bits)."""
-    g_bits = np.asarray(grad_bits, dtype=np.uint16).reshape(-1)
+    g = bf16_to_f32(np.asarray(grad_bits, dtype=np.uint16).reshape(-1))
+    return adamw_step_f32grad(g, master, m, v, step, hp, coef)
+
+
+def adamw_step_f32grad(grad, master, m, v, step: int, hp: AdamWHParams, coef: float):
+    """adamw_step for an fp32 gradient (the fp32-accumulated one)."""
+    g_f32 = np.asarray(grad, dtype=np.float32).reshape(-1)
     master = np.asarray(master, dtype=np.float32).reshape(-1)
     m = np.asarray(m, dtype=np.float32).reshape(-1)
     v = np.asarray(v, dtype=np.float32).reshape(-1)
-    n = g_bits.size
+    n = g_f32.size
     if not (master.size == m.size == v.size == n):
         raise ValueError("shard arrays differ in length")
     out_p = np.empty(n, dtype=np.float32)
@@ -167,7 +200,7 @@ def adamw_step(grad_bits, master, m, v, step: int, hp: AdamWHParams, coef: float
     out_b = np.empty(n, dtype=np.uint16)
     for lo in range(0, n, CHUNK):
         hi = min(n, lo + CHUNK)
-        g_hat = coef * bf16_to_f32(g_bits[lo:hi]).astype(np.float64)
+        g_hat = coef * g_f32[lo:hi].astype(np.float64)
         p1, m1, v1 = adamw_f64(master[lo:hi], m[lo:hi], v[lo:hi], g_hat, step, hp)
         out_p[lo:hi] = p1.astype(np.float32)
         out_m[lo:hi] = m1.astype(np.float32)

@@ -253,3 +253,60 @@ def test_sharded_update_equals_unsharded():
         # divergence the shard-aware rule prevents)
         local = [S.clip_coef(S.sqnorm(s), hp.max_norm) for s in shards]
         assert any(abs(x - c) > 1e-3 for x in local)
+
+
+# ------------------------------------------------ fp32 gradient accumulation
+
+def test_accumulate_matches_torch_fp32_add():
+    rng = np.random.default_rng(41)
+    n = 200_000
+    # accumulators and gradients spanning wide exponent gaps both ways
+    acc = (rng.standard_normal(n) * 10.0 ** rng.uniform(-30, 10, n)).astype(np.float32)
+    g = _rand_bits(rng, n, 1.0)
+    g = np.where(rng.random(n) < 0.5, g,
+                 synth.to_bf16_bits((rng.standard_normal(n) * 10.0 ** rng.uniform(-30, 10, n))
+                                    .astype(np.float32)))
+    ours = S.accumulate(acc, g, first=False)
+    ref = (torch.from_numpy(acc) + torch.from_numpy(g.view(np.int16).copy()).view(torch.bfloat16).float())
+    assert np.array_equal(ours.view(np.uint32), ref.numpy().view(np.uint32))
+    # first micro-batch: exactly the widened gradient
+    first = S.accumulate(np.full(n, np.nan, np.float32), g, first=True)
+    assert np.array_equal(first, bf16_to_f32(g))
+
+
+def test_accumulate_exact_small_integers():
+    ones = np.full(100, 0x3F80, np.uint16)       # 1.0
+    acc = S.accumulate(None, ones, first=True)
+    for _ in range(9):
+        acc = S.accumulate(acc, ones, first=False)
+    assert (acc == 10.0).all()
+
+
+def test_sqnorm_f32_exact():
+    rng = np.random.default_rng(43)
+    x = (rng.standard_normal(3000) * 7.0).astype(np.float32)
+    exact = sum((Fraction(float(v)) ** 2 for v in x), Fraction(0))
+    assert abs(Fraction(S.sqnorm_f32(x)) - exact) <= Fraction(6001) * Fraction(2.0 ** -52) * exact
+    assert S.sqnorm_f32(np.full(777, 3.0, np.float32)) == 9.0 * 777
+    big = np.array([3.0e38, -3.0e38], np.float32)               # squares beyond fp32 range
+    assert S.sqnorm_f32(big) == 2 * float(np.float32(3.0e38)) ** 2
+    assert S.sqnorm_f32(np.zeros(0, np.float32)) == 0.0
+
+
+def test_adamw_f32grad_agrees_with_bf16_path():
+    rng = np.random.default_rng(47)
+    n = 5000
+    bits = _rand_bits(rng, n, 1e-3)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32)
+    hp = S.AdamWHParams()
+    a = S.adamw_step(bits, master, m, v, 4, hp, 0.3)
+    b = S.adamw_step_f32grad(bf16_to_f32(bits), master, m, v, 4, hp, 0.3)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    # a gradient that is not bf16-representable is used as is, not rounded
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    p1, m1, _, _ = S.adamw_step_f32grad(g, master, np.zeros(n, np.float32), np.zeros(n, np.float32),
+                                        1, S.AdamWHParams(weight_decay=0.0, max_norm=0.0), 1.0)
+    assert np.array_equal(m1, (0.1 * g.astype(np.float64)).astype(np.float32))
