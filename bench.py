@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-norm", action="store_true",
                     help="run pack and the sum of squares as two calls instead of the fused one")
+    ap.add_argument("--accum", type=int, default=1, metavar="K",
+                    help="fp32 gradient accumulation over K micro-batches per step (K > 1)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into HBM bytes per launch and exit")
@@ -60,16 +62,35 @@ def kernel_name(raw):
     return name.split("(")[0].split("::")[-1]
 
 
-def algorithmic_bytes(wl):
-    """Algorithmic HBM bytes per launch of each kernel for the whole shard."""
+def algorithmic_bytes(wl, accum=1, separate_norm=False):
+    """Algorithmic HBM bytes per step of each kernel over the whole shard, for
+    the benchmark's mode (fused norm by default, separate norm, or fp32
+    accumulation over ``accum`` micro-batches)."""
     from fsdp_sharded_mixed_zero_amd import zero
     info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
     S = info["shard"]
     real = S - (info["pad_end"] - info["pad_begin"])
-    pad = S - real
-    return S, real, {"copy_pieces_kernel<false>": 4 * real,          # unpack (or unfused pack)
-                     "copy_pieces_kernel<true>": 4 * real + 2 * pad,  # pack + sum of squares
-                     "sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel": 28 * S}
+    pack = 4 * real + 2 * (S - real)
+    out = {"copy_pieces_kernel<false>": 4 * real}          # unpack
+    if accum > 1:
+        out["copy_pieces_kernel<false>"] += accum * pack   # plus one pack per micro-batch
+        out.update({"accumulate_kernel": (6 + 10 * (accum - 1)) * S, "sqnorm_f32_partial_kernel": 4 * S,
+                    "adamw_vec_kernel<float>": 30 * S})
+    else:
+        if separate_norm:
+            out["copy_pieces_kernel<false>"] += pack
+            out["sqnorm_partial_kernel"] = 2 * S
+        else:
+            out["copy_pieces_kernel<true>"] = pack
+        out["adamw_vec_kernel<unsigned short>"] = 28 * S
+    return S, real, out
+
+
+def steps_traced(counts, wl, S):
+    """Steps a trace covers (warm-up included), from the AdamW launches."""
+    pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
+    adamw = next(k for k in counts if k.startswith("adamw_vec_kernel"))
+    return counts[adamw] / pieces
 
 
 def source_hash():
@@ -82,11 +103,11 @@ def traffic_file(workload):
     return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
-def pmc_summary(fetch_dir, write_dir, wl):
+def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
     """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
-    for the copy kernel of known size (copy_pieces_kernel: pack and unpack each
-    read and write 2 bytes per shard element at this workload)."""
+    for the copy kernel of known size (the plain copy_pieces_kernel: unpack
+    reads and writes 2 bytes per real shard element)."""
     import csv
     import glob
 
@@ -101,29 +122,32 @@ def pmc_summary(fetch_dir, write_dir, wl):
 
     fetch, n_f = load(fetch_dir, "FETCH_SIZE")
     write, n_w = load(write_dir, "WRITE_SIZE")
-    S, real, algo = algorithmic_bytes(wl)
+    S, real, algo = algorithmic_bytes(wl, accum, separate_norm)
+    steps = steps_traced(n_f, wl, S)
     # the plain copy (unpack) reads and writes exactly 2 bytes per real element
     copy = "copy_pieces_kernel<false>"
-    known_read = 2 * real / 1024.0        # KiB per dispatch
-    known_write = 2 * real / 1024.0
+    per_dispatch = {k: algo[k] / (n_f[k] / steps) for k in algo if k in n_f}
+    known_read = per_dispatch[copy] / 2 / 1024.0       # KiB per dispatch
+    known_write = per_dispatch[copy] / 2 / 1024.0
     f_fetch = known_read / fetch[copy]
     f_write = known_write / write[copy]
     kernels = {}
     for k in fetch:
-        if k not in algo and k != "sqnorm_final_kernel":
+        if k not in algo and not k.startswith("sqnorm_final"):
             continue
         bytes_ = (fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024.0
         kernels[k] = {"fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
                       "dispatches": n_f[k], "traffic_bytes": int(bytes_),
-                      "algorithmic_bytes": algo.get(k),
-                      "traffic_over_algorithmic": round(bytes_ / algo[k], 4) if k in algo else None}
+                      "algorithmic_bytes": int(per_dispatch[k]) if k in per_dispatch else None,
+                      "traffic_over_algorithmic": round(bytes_ / per_dispatch[k], 4) if k in per_dispatch else None}
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
                 f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o bench -- "
                 f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline",
-                f"python bench.py --workload {wl.name} --pmc-summary {fetch_dir} {write_dir}"],
+                f"python bench.py --workload {wl.name} --steps 20 --warmup 2 "
+                f"--pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
             "kernel_source_sha256": source_hash(),
             "calibration": {"kernel": copy, "known_read_kib": known_read,
@@ -132,7 +156,7 @@ def pmc_summary(fetch_dir, write_dir, wl):
             "kernels": kernels}
 
 
-def stats_summary(stats_dir, wl, steps, warmup):
+def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False):
     """Markdown table of a rocprofv3 kernel-stats CSV of this benchmark, with
     achieved bandwidth from each kernel's algorithmic bytes per launch (the
     step's bytes spread over that kernel's launches per step)."""
@@ -140,16 +164,16 @@ def stats_summary(stats_dir, wl, steps, warmup):
     import glob
 
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
-    S, real, algo = algorithmic_bytes(wl)
+    S, real, algo = algorithmic_bytes(wl, accum, separate_norm)
     rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
-    pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
-    steps_run = int(rows["adamw_vec_kernel"]["Calls"]) / pieces      # warm-up steps included
+    steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S)
+    mode = (f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "")
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
              f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
              "Command (repository root, one MI355X):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o bench -- "
-             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup} --no-cpu-baseline",
-             f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup} "
+             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} --no-cpu-baseline",
+             f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
              f"--stats-summary {stats_dir}", "",
              f"kernels.hip sha256: `{source_hash()}`", "",
              f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "
@@ -158,7 +182,7 @@ def stats_summary(stats_dir, wl, steps, warmup):
              "GB/s at avg | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|---|"]
     for short, row in rows.items():
-        if short not in algo and short != "sqnorm_final_kernel":
+        if short not in algo and not short.startswith("sqnorm_final"):
             continue
         calls = int(row["Calls"])
         per_step = calls / steps_run
@@ -254,12 +278,13 @@ def main():
     args = parse()
     if args.pmc_summary:
         from fsdp_sharded_mixed_zero_amd import synth
-        print(json.dumps(pmc_summary(*args.pmc_summary, synth.WORKLOADS[args.workload]), indent=1))
+        print(json.dumps(pmc_summary(*args.pmc_summary, synth.WORKLOADS[args.workload], args.accum,
+                                     args.separate_norm), indent=1))
         return
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth
-        print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup),
-              end="")
+        print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup,
+                            args.accum, args.separate_norm), end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -276,7 +301,7 @@ def main():
     zero.library()                       # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
-    rs = RankShard(wl, fused_norm=not args.separate_norm)
+    rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum)
     torch.cuda.synchronize()
 
     t = wl.step
@@ -285,7 +310,8 @@ def main():
         t += 1
     torch.cuda.synchronize()
     timing = {}
-    per_step = 2 * (len(rs.pieces()) * (2 if args.separate_norm else 1) + 2 * len(rs.pieces()))
+    n_p = len(rs.pieces())
+    per_step = 2 * (n_p * (2 if args.separate_norm else 1) + 2 * n_p + (3 * args.accum + 1) * n_p)
     events = iter([torch.cuda.Event(enable_timing=True) for _ in range(per_step * args.steps)])
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -306,10 +332,13 @@ def main():
                           "algorithmic_bytes": algo[phase], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
     adamw_launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in timing["adamw"]) / len(timing["adamw"])
-    launch_elems = S / (len(timing["adamw"]) / args.steps)
-    achieved = 28 * launch_elems / (adamw_launch_ms * 1e-3) / 1e9
+    adamw_launches = len(timing["adamw"]) / args.steps
+    launch_elems = S / adamw_launches
+    launch_bytes = algo["adamw"] / adamw_launches
+    achieved = launch_bytes / (adamw_launch_ms * 1e-3) / 1e9
     step_bytes = sum(algo.values())
-    traffic = measured_traffic(wl.name, "adamw_vec_kernel") if rs.bucket <= 0 else None
+    default_kernel = rs.bucket <= 0 and args.accum == 1
+    traffic = measured_traffic(wl.name, "adamw_vec_kernel<unsigned short>") if default_kernel else None
 
     out = {
         "metric": "fused sharded AdamW params/sec/GPU + achieved HBM GB/s (% of MI355X peak)",
@@ -328,13 +357,14 @@ def main():
                                f"pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack",
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
                    "segments_in_shard": len(rs.segments), "adamw_step": wl.step,
-                   "bucket": rs.bucket, "norm": "separate" if args.separate_norm else "fused into pack"},
+                   "bucket": rs.bucket, "norm": "separate" if args.separate_norm else "fused into pack",
+                   "fp32_grad_accumulation_micro_batches": args.accum if args.accum > 1 else None},
         "adamw_params_per_s": launch_elems / (adamw_launch_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(28 * launch_elems)},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(launch_bytes)},
     }
     del rs
     torch.cuda.empty_cache()

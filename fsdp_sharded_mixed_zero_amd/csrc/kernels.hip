@@ -370,6 +370,46 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(const uint16
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
+// fp32 gradients: the same tiles of kSqVecPerBlock * 8 = 4096 elements per
+// block (so the block count and workspace are those of the bf16 kernel), each
+// lane loading four 16-byte vectors of 4 floats.
+__device__ __forceinline__ double sq4(f32x4 w, double acc) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double a = double(w[k]);
+    acc = fma(a, a, acc);
+  }
+  return acc;
+}
+
+__global__ __launch_bounds__(kSqThreads) void sqnorm_f32_partial_kernel(const float* __restrict__ g, int64_t count,
+                                                                         int64_t head, double* __restrict__ partial) {
+  constexpr int VPT = 4;
+  constexpr int64_t VPB = int64_t(kSqThreads) * VPT;   // 1024 vectors = 4096 floats
+  const int64_t nvec = (count - head) >> 2;
+  const f32x4* __restrict__ gv = reinterpret_cast<const f32x4*>(g + head);
+  double acc = 0.0;
+  for (int64_t tile = blockIdx.x; tile * VPB < nvec; tile += gridDim.x) {
+    const int64_t i0 = tile * VPB + threadIdx.x;
+    f32x4 r[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t i = i0 + int64_t(k) * kSqThreads;
+      r[k] = i < nvec ? __builtin_nontemporal_load(gv + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) acc = sq4(r[k], acc);
+  }
+  if (blockIdx.x == 0) {
+    const int t = threadIdx.x;
+    if (t < head) acc = fma(double(g[t]), double(g[t]), acc);
+    const int64_t k = head + nvec * 4 + (t - 4);
+    if (t >= 4 && k < count) acc = fma(double(g[k]), double(g[k]), acc);
+  }
+  const double s = block_sum<kSqThreads>(acc);
+  if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
 __global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const double* __restrict__ partial,
                                                                         int64_t n, double* __restrict__ out,
                                                                         int accumulate) {
@@ -414,7 +454,7 @@ static_assert(kTile == ZERO_STATE_TILE, "state tile size");
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct AdamWArgs {
-  const uint16_t* g;      // shard element 0
+  const void* g;          // shard element 0 (bf16 bits, or fp32 for the accumulated gradient)
   float* state;           // shard element 0's tile
   uint16_t* param;        // shard element 0
   int64_t n_state;        // elements the state buffer describes
@@ -455,17 +495,36 @@ __device__ __forceinline__ float* tile_slot(const AdamWArgs& a, int64_t e, int64
   return a.state + 3 * k0 + (e - k0);
 }
 
+template <typename G>
+__device__ __forceinline__ float grad_at(const AdamWArgs& a, int64_t e) {
+  if constexpr (sizeof(G) == 2) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.g)[e]) << 16);
+  else return static_cast<const float*>(a.g)[e];
+}
+
+// The 4 gradients of the unit at element e (a multiple of 4).
+template <typename G>
+__device__ __forceinline__ f32x4 grad4(const AdamWArgs& a, int64_t e) {
+  if constexpr (sizeof(G) == 2) {
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.g) + e));
+    return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(a.g) + e));
+  }
+}
+
+template <typename G>
 __device__ __forceinline__ void adamw_scalar(const AdamWArgs& a, float c, int64_t e) {
   int64_t L;
   float* s = tile_slot(a, e, &L);
   float p = s[0], m = s[L], v = s[2 * L];
-  adamw_one(a, c, __uint_as_float(uint32_t(a.g[e]) << 16), p, m, v);
+  adamw_one(a, c, grad_at<G>(a, e), p, m, v);
   s[0] = p;
   s[L] = m;
   s[2 * L] = v;
   a.param[e] = to_bf16(p);
 }
 
+template <typename G>
 __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs a) {
   const float c = clip_coefficient(a);
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
@@ -474,13 +533,13 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs
     int64_t L;
     float* s = tile_slot(a, e, &L);
     if (L & 3) {   // a compact last tile whose m and v are not 16-byte aligned
-      for (int k = 0; k < 4; ++k) adamw_scalar(a, c, e + k);
+      for (int k = 0; k < 4; ++k) adamw_scalar<G>(a, c, e + k);
       continue;
     }
     f32x4* ps = reinterpret_cast<f32x4*>(s);
     f32x4* ms = reinterpret_cast<f32x4*>(s + L);
     f32x4* vs = reinterpret_cast<f32x4*>(s + 2 * L);
-    const u32x2 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.g + e));
+    const f32x4 g4 = grad4<G>(a, e);
     const f32x4 p4 = __builtin_nontemporal_load(ps);
     const f32x4 m4 = __builtin_nontemporal_load(ms);
     const f32x4 v4 = __builtin_nontemporal_load(vs);
@@ -488,10 +547,7 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs
     float m[4] = {m4[0], m4[1], m4[2], m4[3]};
     float v[4] = {v4[0], v4[1], v4[2], v4[3]};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float g = (k & 1) ? bf16_hi(gw[k >> 1]) : bf16_lo(gw[k >> 1]);
-      adamw_one(a, c, g, p[k], m[k], v[k]);
-    }
+    for (int k = 0; k < 4; ++k) adamw_one(a, c, g4[k], p[k], m[k], v[k]);
     __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, ps);
     __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, ms);
     __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, vs);
@@ -502,18 +558,47 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs
   if (blockIdx.x == 0) {
     const int t = threadIdx.x;
     const int64_t head_end = 4 * a.u_begin < a.end ? 4 * a.u_begin : a.end;
-    if (t < 4 && a.begin + t < head_end) adamw_scalar(a, c, a.begin + t);
+    if (t < 4 && a.begin + t < head_end) adamw_scalar<G>(a, c, a.begin + t);
     const int64_t k = 4 * a.u_end + (t - 4);
-    if (t >= 4 && t < 8 && k >= head_end && k < a.end) adamw_scalar(a, c, k);
+    if (t >= 4 && t < 8 && k >= head_end && k < a.end) adamw_scalar<G>(a, c, k);
   }
 }
 
 // Element path for base pointers without the vector path's alignment.
+template <typename G>
 __global__ __launch_bounds__(kAdamThreads) void adamw_elem_kernel(const AdamWArgs a) {
   const float c = clip_coefficient(a);
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
   for (int64_t e = a.begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; e < a.end; e += stride)
-    adamw_scalar(a, c, e);
+    adamw_scalar<G>(a, c, e);
+}
+
+// ------------------------------------------------ fp32 gradient accumulation
+// acc = (first ? 0 : acc) + g for one micro-batch: an 8-byte bf16 load and a
+// 16-byte fp32 load/store per lane (4 elements), fp32 add (round to nearest).
+
+__global__ __launch_bounds__(kAdamThreads) void accumulate_kernel(const uint16_t* __restrict__ g,
+                                                                   float* __restrict__ acc, int64_t count,
+                                                                   int first, int vec) {
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  const int64_t units = vec ? (count >> 2) : count;
+  for (int64_t u = int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < units; u += stride) {
+    if (vec) {
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g) + u);
+      f32x4* ap = reinterpret_cast<f32x4*>(acc) + u;
+      const f32x4 x = {bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      const f32x4 r = first ? x : __builtin_nontemporal_load(ap) + x;
+      __builtin_nontemporal_store(r, ap);
+    } else {
+      const float x = __uint_as_float(uint32_t(g[u]) << 16);
+      acc[u] = first ? x : acc[u] + x;
+    }
+  }
+  if (vec && blockIdx.x == 0 && threadIdx.x < (count & 3)) {   // the last count % 4 elements
+    const int64_t e = ((count >> 2) << 2) + threadIdx.x;
+    const float x = __uint_as_float(uint32_t(g[e]) << 16);
+    acc[e] = first ? x : acc[e] + x;
+  }
 }
 
 // ------------------------------------------------ state layout conversion
@@ -668,10 +753,10 @@ extern "C" int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* 
   return zero::ok();
 }
 
-extern "C" int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
-                               int64_t begin, int64_t count, const zero_adamw_hparams* hp,
-                               const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream) {
-  static const char* who = "zero_adamw_step";
+template <typename G>
+static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
+                        int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
+                        int32_t n_ranks, hipStream_t stream, const char* who) {
   if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
   if (n_state < 0 || begin < 0 || count < 0 || begin > n_state || count > n_state - begin)
     return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside a state of %lld elements", who, (long long)begin,
@@ -682,7 +767,7 @@ extern "C" int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t*
     return fail(ZERO_EINVAL, "%s: clipping needs the ranks' sums of squares", who);
   if (count == 0) return zero::ok();
   if (!d_grad || !d_state || !d_param) return fail(ZERO_EINVAL, "%s: NULL buffer", who);
-  if (((uintptr_t(d_grad) | uintptr_t(d_param)) & 1u) || (uintptr_t(d_state) & 3u))
+  if ((uintptr_t(d_grad) & (sizeof(G) - 1)) || (uintptr_t(d_param) & 1u) || (uintptr_t(d_state) & 3u))
     return fail(ZERO_EINVAL, "%s: misaligned element pointer", who);
 
   AdamWArgs a{};
@@ -712,14 +797,70 @@ extern "C" int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t*
   a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
   a.eps = float(hp->eps);
 
-  const bool vec = aligned(d_grad, 8) && aligned(d_param, 8) && aligned(d_state, 16);
+  // vector path: 4 gradients (8 or 16 bytes), 4 bf16 params (8 bytes), fp32 state (16 bytes)
+  const bool vec = aligned(d_grad, 4 * sizeof(G)) && aligned(d_param, 8) && aligned(d_state, 16);
   const int64_t work = vec ? std::max<int64_t>(a.u_end - a.u_begin, 1) : count;
   int64_t blocks = (work + kAdamThreads - 1) / kAdamThreads;
   blocks = std::min(std::max<int64_t>(blocks, 1), kAdamMaxBlocks);
   if (vec)
-    hipLaunchKernelGGL(adamw_vec_kernel, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+    hipLaunchKernelGGL(adamw_vec_kernel<G>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(adamw_elem_kernel, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+    hipLaunchKernelGGL(adamw_elem_kernel<G>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_shard_sqnorm_f32(const float* d_grad, int64_t count, double* d_out, int32_t accumulate,
+                                     void* d_workspace, size_t ws_bytes, hipStream_t stream) {
+  static const char* who = "zero_shard_sqnorm_f32";
+  if (count < 0) return fail(ZERO_EINVAL, "%s: count < 0", who);
+  if (d_out == nullptr || d_workspace == nullptr) return fail(ZERO_EINVAL, "%s: NULL output or workspace", who);
+  if (count > 0 && d_grad == nullptr) return fail(ZERO_EINVAL, "%s: NULL gradient", who);
+  if (uintptr_t(d_grad) & 3u) return fail(ZERO_EINVAL, "%s: gradient pointer is not 4-byte aligned", who);
+  if (uintptr_t(d_workspace) & 7u) return fail(ZERO_EINVAL, "%s: workspace is not 8-byte aligned", who);
+  const int nb = sq_blocks(count);
+  if (ws_bytes < size_t(nb) * sizeof(double))
+    return fail(ZERO_EINVAL, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, size_t(nb) * sizeof(double));
+  double* part = static_cast<double*>(d_workspace);
+  // floats before the first 16-byte boundary
+  const int64_t head = std::min<int64_t>(count, int64_t(((16u - (uintptr_t(d_grad) & 15u)) & 15u) >> 2));
+  hipLaunchKernelGGL(sqnorm_f32_partial_kernel, dim3(nb), dim3(kSqThreads), 0, stream, d_grad, count, head, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, part, int64_t(nb), d_out,
+                     accumulate ? 1 : 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                               int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                               const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream) {
+  return adamw_launch<uint16_t>(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks,
+                                stream, "zero_adamw_step");
+}
+
+extern "C" int zero_adamw_step_f32grad(const float* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                                       int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                                       const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream) {
+  return adamw_launch<float>(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks,
+                             stream, "zero_adamw_step_f32grad");
+}
+
+extern "C" int zero_accumulate_grads(const uint16_t* d_grad, float* d_acc, int64_t count, int32_t first,
+                                     hipStream_t stream) {
+  static const char* who = "zero_accumulate_grads";
+  if (count < 0) return fail(ZERO_EINVAL, "%s: count < 0", who);
+  if (count == 0) return zero::ok();
+  if (!d_grad || !d_acc) return fail(ZERO_EINVAL, "%s: NULL buffer", who);
+  if ((uintptr_t(d_grad) & 1u) || (uintptr_t(d_acc) & 3u)) return fail(ZERO_EINVAL, "%s: misaligned pointer", who);
+  const bool vec = aligned(d_grad, 8) && aligned(d_acc, 16);
+  const int64_t units = vec ? std::max<int64_t>(count >> 2, 1) : count;
+  const int64_t blocks = std::min(std::max<int64_t>((units + kAdamThreads - 1) / kAdamThreads, 1), kAdamMaxBlocks);
+  hipLaunchKernelGGL(accumulate_kernel, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, d_grad, d_acc, count,
+                     first ? 1 : 0, vec ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return zero::ok();

@@ -15,7 +15,10 @@ hold them), the flat bf16 gradient and parameter shards, the fp32 state
 (master, m, v: one 12 B/element buffer in the library's tiled layout), the
 ranks' partial sums and the sum-of-squares workspace. With ``bucket`` > 0
 the shard is processed in pieces of that many elements, a constant-size
-working set (notes, section 5.2).
+working set (notes, section 5.2). With ``accum_steps`` = K > 1 the step runs
+K micro-batches of pack + fp32 accumulation, then the norm and AdamW on the
+fp32 accumulator ("第 5 课：ZeRO 与 FSDP" section 2, fp32 gradient
+accumulation, 4 extra bytes per shard element).
 """
 
 from __future__ import annotations
@@ -27,7 +30,8 @@ from . import synth, zero
 
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
-                 fill: bool = True, bucket: int | None = None, fused_norm: bool = True):
+                 fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
+                 accum_steps: int = 1):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -54,6 +58,8 @@ class RankShard:
         self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
         self.fused_norm = fused_norm
+        self.accum_steps = accum_steps
+        self.acc = torch.empty(S, dtype=torch.float32, device=dev) if accum_steps > 1 else None
         ws = max(max(zero.zero_sqnorm_workspace_bytes(n),
                      zero.zero_pack_sqnorm_workspace_bytes(self.layout, b, n)) for b, n in self.pieces())
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=dev)
@@ -118,12 +124,13 @@ class RankShard:
             return [(0, self.shard)]
         return [(b, min(self.bucket, self.shard - b)) for b in range(0, self.shard, self.bucket)]
 
-    def step(self, step, stream=None, timing=None, events=None):
+    def step(self, step, stream=None, timing=None, events=None, before_micro=None):
         """One local step. ``timing``: optional dict; each phase ("pack_sqnorm"
         or "pack" and "sqnorm", "adamw", "unpack") gets a list of (start, end)
         CUDA events recorded around its launches on the current stream, taken
         from the iterator ``events`` (pre-created, so timing adds no event
-        creation to the step)."""
+        creation to the step). ``before_micro(mb)`` runs before each
+        micro-batch when accumulating (to refill the gradients)."""
         hp = self.hparams(step)
         own = self.rank_sq[self.rank:self.rank + 1]
         pieces = self.pieces()
@@ -141,6 +148,9 @@ class RankShard:
             e1.record()
             timing.setdefault(phase, []).append((e0, e1))
 
+        if self.accum_steps > 1:
+            self._step_accumulated(hp, own, pieces, stream, mark, before_micro)
+            return
         for k, (b, n) in enumerate(pieces):
             if self.fused_norm:
                 mark("pack_sqnorm", lambda: zero.zero_pack_grads_sqnorm(
@@ -158,12 +168,38 @@ class RankShard:
             mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
 
+    def _step_accumulated(self, hp, own, pieces, stream, mark, before_micro):
+        for mb in range(self.accum_steps):
+            if before_micro is not None:
+                before_micro(mb)
+            for b, n in pieces:
+                mark("pack", lambda: zero.zero_pack_grads(self.layout, self.grad_ptrs, self.grad_shard, b, n,
+                                                          stream))
+                mark("accumulate", lambda: zero.zero_accumulate_grads(self.grad_shard[b:], self.acc[b:], n,
+                                                                      mb == 0, stream))
+        for k, (b, n) in enumerate(pieces):
+            mark("sqnorm", lambda: zero.zero_shard_sqnorm_f32(self.acc[b:], n, own, k > 0, self.workspace,
+                                                              stream=stream))
+        for b, n in pieces:
+            mark("adamw", lambda: zero.zero_adamw_step_f32grad(
+                self.acc, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                self.wl.n_d, stream))
+            mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
+                                                          b, n, stream))
+
     def bytes_per_step(self):
         """Algorithmic HBM bytes of one step: pack 4, sum of squares 2 (0 when
         fused into pack), AdamW 28 and unpack 4 bytes per shard element (pack
-        writes only 2 on padding, unpack moves nothing there)."""
+        writes only 2 on padding, unpack moves nothing there). Accumulating K
+        micro-batches: K packs, accumulation 6 then 10 bytes per element, an
+        fp32 norm (4) and AdamW on fp32 gradients (30)."""
         pad = self.shard - self.real
         pack = 4 * self.real + 2 * pad
+        if self.accum_steps > 1:
+            K, S = self.accum_steps, self.shard
+            # accumulate: 2 + 4 bytes for the first micro-batch, 2 + 4 + 4 after
+            return {"pack": K * pack, "accumulate": 6 * S + (K - 1) * 10 * S, "sqnorm": 4 * S,
+                    "adamw": 30 * S, "unpack": 4 * self.real}
         out = {"adamw": 28 * self.shard, "unpack": 4 * self.real}
         if self.fused_norm:
             out["pack_sqnorm"] = pack

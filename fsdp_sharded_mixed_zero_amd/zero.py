@@ -78,6 +78,10 @@ _SIGNATURES = {
     "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                        ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
+    "zero_adamw_step_f32grad": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
+                                               ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
+    "zero_accumulate_grads": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
+    "zero_shard_sqnorm_f32": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_state_import": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
     "zero_state_export": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
     "zero_unpack_params": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_VP), _I64, _I64, _VP]),
@@ -247,6 +251,27 @@ def zero_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp
     _check("zero_adamw_step", library().zero_adamw_step(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count: int,
+                            hp: zero_adamw_hparams, rank_sqnorms, n_ranks: int, stream=None):
+    _check("zero_adamw_step_f32grad", library().zero_adamw_step_f32grad(
+        _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def zero_accumulate_grads(grad, acc, count: int, first: bool, stream=None):
+    _check("zero_accumulate_grads", library().zero_accumulate_grads(
+        _ptr(grad), _ptr(acc), count, 1 if first else 0, _stream(stream)))
+
+
+def zero_shard_sqnorm_f32(grad, count: int, out, accumulate: bool, workspace, ws_bytes: int | None = None,
+                          stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("zero_shard_sqnorm_f32", library().zero_shard_sqnorm_f32(
+        _ptr(grad), count, _ptr(out), 1 if accumulate else 0, _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def zero_state_import(master, m, v, state, n: int, stream=None):

@@ -254,6 +254,36 @@ int zero_state_export(const float* d_state, float* d_master, float* d_m, float* 
                       hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * fp32 gradient accumulation ("第 5 课：ZeRO 与 FSDP" section 2, note on fp32
+ * gradient accumulation: with ZeRO-2/3 the accumulator is partitioned like
+ * the gradients, 4 bytes per shard element).
+ *
+ * zero_accumulate_grads -- d_acc[i] = (first ? 0 : d_acc[i]) + g[i] for count
+ * elements: one micro-batch's bf16 gradient slice added into the fp32
+ * accumulator (fp32 add, round to nearest even; with first != 0 d_acc is not
+ * read). Sub-ranges by offset pointers. 8-byte aligned d_grad and 16-byte
+ * aligned d_acc take the vector path. Errors: ZERO_EINVAL for count < 0, NULL
+ * buffers (allowed when count == 0) or pointers not aligned to their element
+ * size; ZERO_EHIP if a launch fails. */
+int zero_accumulate_grads(const uint16_t* d_grad, float* d_acc, int64_t count, int32_t first,
+                          hipStream_t stream);
+
+/* zero_shard_sqnorm_f32 -- zero_shard_sqnorm for an fp32 gradient (the
+ * accumulator): *d_out (+)= sum of g*g, each square exact in fp64, fixed
+ * order. The workspace is zero_sqnorm_workspace_bytes(count) bytes. Errors as
+ * zero_shard_sqnorm (d_grad must be 4-byte aligned). */
+int zero_shard_sqnorm_f32(const float* d_grad, int64_t count, double* d_out, int32_t accumulate,
+                          void* d_workspace, size_t ws_bytes, hipStream_t stream);
+
+/* zero_adamw_step_f32grad -- zero_adamw_step with an fp32 gradient shard
+ * (d_grad: element 0 of the accumulator): the same update and arguments,
+ * 30 bytes per element instead of 28. The vector path needs d_grad 16-byte
+ * aligned. Errors as zero_adamw_step. */
+int zero_adamw_step_f32grad(const float* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                            int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                            const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * zero_unpack_params -- write the updated bf16 shard back into the tensors.
  * Copies shard elements [begin, begin+count) of param_shard to the tensor
  * elements the layout maps them to (the full parameters that the all-gather

@@ -301,21 +301,30 @@ def _inputs(n, m_std, v_std, seed):
     return bits, master, m, v
 
 
-def _adamw_case(n, begin, count, step, ohp, n_ranks, m_std, v_std, seed, misalign=False):
+def _adamw_case(n, begin, count, step, ohp, n_ranks, m_std, v_std, seed, misalign=False, f32grad=False):
     """Update elements [begin, begin+count) of an n-element shard; with
-    ``misalign`` every base pointer is shifted off its vector alignment."""
+    ``misalign`` every base pointer is shifted off its vector alignment; with
+    ``f32grad`` the gradient is fp32 (not bf16-representable)."""
     rng = np.random.default_rng(seed + 1)
     bits, master, m, v = _inputs(n, m_std, v_std, seed)
     parts = np.abs(rng.standard_normal(n_ranks)) * 3e-4 * max(n, 1)
     sh = 1 if misalign else 0
-    d_g = to_dev_u16(np.concatenate([np.zeros(sh, np.uint16), bits]))[sh:]
+    if f32grad:
+        g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        d_g = to_dev_f32(np.concatenate([np.zeros(sh, np.float32), g32]))[sh:]
+    else:
+        d_g = to_dev_u16(np.concatenate([np.zeros(sh, np.uint16), bits]))[sh:]
     d_s = to_dev_f32(np.concatenate([np.zeros(sh, np.float32), to_tiles(master, m, v)]))[sh:]
     d_o = sentinel(n + 1)[sh:sh + n]
     d_parts = torch.from_numpy(parts).to(DEV)
-    zero.zero_adamw_step(d_g, d_s, d_o, n, begin, count, hp_of(ohp, step), d_parts, n_ranks)
+    step_fn = zero.zero_adamw_step_f32grad if f32grad else zero.zero_adamw_step
+    step_fn(d_g, d_s, d_o, n, begin, count, hp_of(ohp, step), d_parts, n_ranks)
     coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
     sl = slice(begin, begin + count)
-    want = O.adamw_step(bits[sl], master[sl], m[sl], v[sl], step, ohp, coef)
+    if f32grad:
+        want = O.adamw_step_f32grad(g32[sl], master[sl], m[sl], v[sl], step, ohp, coef)
+    else:
+        want = O.adamw_step(bits[sl], master[sl], m[sl], v[sl], step, ohp, coef)
     g_master, g_m, g_v = from_tiles(d_s.cpu().numpy(), n)
     g_o = to_host_u16(d_o)
     # nothing outside the range moved
@@ -420,3 +429,56 @@ def test_state_import_export(n, misalign):
     zero.zero_state_export(d_state, *outs, n)
     for o, x in zip(outs, (master, m, v)):
         assert np.array_equal(o.cpu().numpy(), x)
+
+
+# ------------------------------------------------ fp32 gradient accumulation
+
+@pytest.mark.parametrize("n", [1, 5, 8, 1000, 65_536 + 3, 1_000_003])
+@pytest.mark.parametrize("misalign", [False, True])
+def test_accumulate_grads(n, misalign):
+    """Three micro-batches of bf16 gradients with very different scales added
+    into the fp32 accumulator: bit-exact with the oracle after each."""
+    rng = np.random.default_rng(n + misalign)
+    sh = 1 if misalign else 0
+    acc = to_dev_f32(np.full(n + 4, np.nan, np.float32))[sh:sh + n]    # NaN: must not be read first
+    o_acc = None
+    for mb, scale in enumerate((1e-3, 1e2, 1e-8)):
+        bits = synth.to_bf16_bits((rng.standard_normal(n) * scale).astype(np.float32))
+        d_bits = to_dev_u16(np.concatenate([np.zeros(sh, np.uint16), bits]))[sh:]
+        zero.zero_accumulate_grads(d_bits, acc, n, mb == 0)
+        o_acc = O.accumulate(o_acc, bits, first=(mb == 0))
+        assert np.array_equal(acc.cpu().numpy().view(np.uint32), o_acc.view(np.uint32)), mb
+
+
+@pytest.mark.parametrize("count", [0, 1, 3, 4, 5, 4095, 4096 * 3 + 7, 1 << 20, 3_000_017])
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_sqnorm_f32(count, offset):
+    rng = np.random.default_rng(count * 3 + offset)
+    x = (rng.standard_normal(count + offset) * 10.0 ** rng.uniform(-8, 3, count + offset)).astype(np.float32)
+    d = to_dev_f32(x)
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ws = torch.empty(zero.zero_sqnorm_workspace_bytes(count) // 8, dtype=torch.float64, device=DEV)
+    zero.zero_shard_sqnorm_f32(d[offset:], count, out, False, ws)
+    got = float(out.cpu()[0])
+    want = O.sqnorm_f32(x[offset:])
+    if count == 0:
+        assert got == 0.0
+    else:
+        assert abs(got - want) <= 1e-12 * want
+    zero.zero_shard_sqnorm_f32(d[offset:], count, out, True, ws)
+    assert float(out.cpu()[0]) == 2 * got
+
+
+@pytest.mark.parametrize("n", [1, 9, TILE + 5, 3 * TILE + 6, 300_001])
+@pytest.mark.parametrize("misalign", [False, True])
+def test_adamw_f32grad(n, misalign):
+    ohp = O.AdamWHParams()
+    _check_adamw(*_adamw_case(n, 0, n, 5, ohp, 4, 1e-4, 1e-8, seed=n + 11, misalign=misalign,
+                              f32grad=True))
+
+
+@pytest.mark.parametrize("begin,count", [(1, 8), (TILE - 2, 9), (4, 3 * TILE), (2 * TILE + 1, 3)])
+def test_adamw_f32grad_sub_ranges(begin, count):
+    n = 3 * TILE + 10
+    _check_adamw(*_adamw_case(n, begin, count, 2, O.AdamWHParams(), 2, 1e-4, 1e-8,
+                              seed=begin + count, f32grad=True))

@@ -171,3 +171,67 @@ def test_workload_full_size(name, fused_norm):
     print(f"[{name}] clip coefficient {coef:.6g}; checks passed", flush=True)
     del rs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,micro", [("gpt2-1.5b", 3), ("gpt-7.5b", 4)])
+def test_workload_grad_accumulation(name, micro):
+    """fp32 gradient accumulation over several micro-batches at full size:
+    the whole accumulator bit-exact with the oracle's, the fp32 norm against
+    the oracle's, AdamW on sampled ranges."""
+    from fsdp_sharded_mixed_zero_amd.rank import RankShard
+
+    wl = synth.WORKLOADS[name]
+    lay = build_layout(wl.sizes, wl.n_d, wl.rank, wl.align)
+    S = lay.shard
+    rng = np.random.default_rng(7 + len(wl.sizes))
+    ranges = sample_ranges(lay, wl, rng)
+    print(f"\n[{name} x{micro}] shard {S}, fp32 accumulation over {micro} micro-batches", flush=True)
+    rs = RankShard(wl, fill=False, accum_steps=micro)
+    before = {}
+
+    def capture(lo, hi, master, m, v):
+        for b, c in ranges:
+            a, z = max(b, lo), min(b + c, hi)
+            if a < z:
+                before.setdefault(b, []).append((a, master[a - lo:z - lo].cpu().numpy(),
+                                                 m[a - lo:z - lo].cpu().numpy(),
+                                                 v[a - lo:z - lo].cpu().numpy()))
+
+    rs.fill_state(on_chunk=capture)
+    rs.fill_other_ranks()
+    others = rs.rank_sq.cpu().numpy().copy()
+    lazy = [None if t is None else DeviceTensor(t) for t in rs.grads]
+    o_acc = [None]
+
+    def before_micro(mb):
+        rs.fill_grads(100 + mb)                       # a different gradient per micro-batch
+        torch.cuda.synchronize()
+        o_acc[0] = O.accumulate(o_acc[0], O.pack(lay, lazy, 0, S), first=(mb == 0))
+
+    rs.step(wl.step, before_micro=before_micro)
+    torch.cuda.synchronize()
+    acc = o_acc[0]
+    assert np.array_equal(rs.acc.cpu().numpy().view(np.uint32), acc.view(np.uint32))
+    got = float(rs.rank_sq[rs.rank].cpu())
+    want = O.sqnorm_f32(acc)
+    rel = assert_norm_close(got, want, f"{name} fp32 partial")
+    print(f"[{name} x{micro}] accumulator bit-exact; partial relative error {rel:.2e}", flush=True)
+    partials = others.copy()
+    partials[rs.rank] = want
+    coef = O.clip_coef(O.global_sqnorm(partials), wl.max_norm)
+    ohp = O.AdamWHParams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                         weight_decay=wl.weight_decay, max_norm=wl.max_norm)
+    for b, c in ranges:
+        pieces = sorted(before[b], key=lambda x: x[0])
+        master = np.concatenate([p[1] for p in pieces])
+        m = np.concatenate([p[2] for p in pieces])
+        v = np.concatenate([p[3] for p in pieces])
+        o_master, o_m, o_v, o_param = O.adamw_step_f32grad(acc[b:b + c], master, m, v, wl.step, ohp, coef)
+        g_master, g_m, g_v = state_range(lambda a, z: rs.state[a:z].cpu().numpy(), S, b, c)
+        assert_f32_state(g_master, o_master, f"{name} master @{b}")
+        assert_f32_state(g_m, o_m, f"{name} m @{b}", m)
+        assert_f32_state(g_v, o_v, f"{name} v @{b}", v)
+        assert_bf16_param(u16(rs.param_shard[b:b + c]), o_param, o_master, f"{name} param @{b}", g_master)
+    print(f"[{name} x{micro}] clip coefficient {coef:.6g}; checks passed", flush=True)
+    del rs
+    torch.cuda.empty_cache()
