@@ -124,13 +124,14 @@ class RankShard:
             return [(0, self.shard)]
         return [(b, min(self.bucket, self.shard - b)) for b in range(0, self.shard, self.bucket)]
 
-    def step(self, step, stream=None, timing=None, events=None, before_micro=None):
+    def step(self, step, stream=None, timing=None, events=None, before_micro=None, phases=None):
         """One local step. ``timing``: optional dict; each phase ("pack_sqnorm"
         or "pack" and "sqnorm", "adamw", "unpack") gets a list of (start, end)
         CUDA events recorded around its launches on the current stream, taken
         from the iterator ``events`` (pre-created, so timing adds no event
-        creation to the step). ``before_micro(mb)`` runs before each
-        micro-batch when accumulating (to refill the gradients)."""
+        creation to the step); ``phases`` limits the timed phases (each event
+        record costs GPU time between launches). ``before_micro(mb)`` runs
+        before each micro-batch when accumulating (to refill the gradients)."""
         hp = self.hparams(step)
         own = self.rank_sq[self.rank:self.rank + 1]
         pieces = self.pieces()
@@ -138,7 +139,7 @@ class RankShard:
             stream = torch.cuda.current_stream().cuda_stream
 
         def mark(phase, fn):
-            if timing is None:
+            if timing is None or (phases is not None and phase not in phases):
                 fn()
                 return
             e0 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
