@@ -483,8 +483,9 @@ __device__ __forceinline__ void adamw_one(const AdamWArgs& a, float c, float g, 
   m = fmaf(a.beta1, m, a.omb1 * gh);
   v = fmaf(a.beta2, v, a.omb2 * (gh * gh));
   const float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
-  const float upd = a.step_size * (m / denom);
-  p = fmaf(-a.lr_wd, p, p) - upd;
+  // decoupled decay first, then the step: p - lr*wd*p - step_size*(m/denom),
+  // each as one fused multiply-add (the host update runs the same sequence)
+  p = fmaf(-a.step_size, m / denom, fmaf(-a.lr_wd, p, p));
 }
 
 // Position of element e's master value in the state buffer and its tile length.

@@ -1,0 +1,161 @@
+// Host-side AdamW for ZeRO-Offload: the rank's fp32 optimizer state lives in
+// host memory and the host cores run the update, while the GPU keeps the bf16
+// gradient and parameter shards (the mlqm.cn article's ZeRO-Offload section:
+// optimizer state moved to CPU memory, the CPU performs the Adam update, the
+// results travel back over PCIe; "別再複製本可分片的東西" mentions CPU and NVMe
+// offload of the sharded state).
+//
+// The update is the same fp32 operation sequence as the GPU kernel (fused
+// multiply-adds, correctly rounded square root and division, round-to-nearest-
+// even bf16 cast), on the same tiled state layout, so the offloaded step and
+// the GPU step agree bit for bit on hosts with hardware FMA. Work is split
+// across threads by whole elements ranges; each thread walks the tiles its
+// range meets and runs a contiguous, vectorisable loop per tile. The inner
+// loop is compiled for AVX-512, AVX2+FMA and baseline x86-64 and picked at run
+// time.
+#include <sched.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "zero_internal.h"
+
+using zero::fail;
+
+namespace {
+
+constexpr int64_t kTile = ZERO_STATE_TILE;
+
+struct HostAdam {
+  float beta1, omb1, beta2, omb2, lr_wd, step_size, inv_sqrt_bc2, eps, coef;
+};
+
+inline uint16_t bf16_rne(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x0040u);   // quiet NaN, sign kept
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+inline float widen(uint16_t h) {
+  const uint32_t u = uint32_t(h) << 16;
+  float x;
+  std::memcpy(&x, &u, 4);
+  return x;
+}
+
+// One contiguous run of n elements: gradients g[0..n), state slots p/m/v
+// (stride 1), parameters out[0..n).
+__attribute__((target_clones("arch=x86-64-v4", "arch=x86-64-v3", "default")))
+void adam_run(const HostAdam& a, const uint16_t* __restrict g, float* __restrict p, float* __restrict m,
+              float* __restrict v, uint16_t* __restrict out, int64_t n) {
+  for (int64_t j = 0; j < n; ++j) {
+    const float gh = widen(g[j]) * a.coef;
+    const float mj = std::fma(a.beta1, m[j], a.omb1 * gh);
+    const float vj = std::fma(a.beta2, v[j], a.omb2 * (gh * gh));
+    const float denom = std::fma(std::sqrt(vj), a.inv_sqrt_bc2, a.eps);
+    const float pj = std::fma(-a.step_size, mj / denom, std::fma(-a.lr_wd, p[j], p[j]));
+    m[j] = mj;
+    v[j] = vj;
+    p[j] = pj;
+    out[j] = bf16_rne(pj);
+  }
+}
+
+// Elements [lo, hi) of the shard; g and param hold the call's range, which
+// starts at element `begin`.
+void adam_range(const HostAdam& a, const uint16_t* g, float* state, uint16_t* param, int64_t n_state,
+                int64_t begin, int64_t lo, int64_t hi) {
+  int64_t e = lo;
+  while (e < hi) {
+    const int64_t k0 = (e / kTile) * kTile;
+    const int64_t L = std::min(kTile, n_state - k0);
+    const int64_t stop = std::min(hi, k0 + L);
+    float* base = state + 3 * k0 + (e - k0);
+    adam_run(a, g + (e - begin), base, base + L, base + 2 * L, param + (e - begin), stop - e);
+    e = stop;
+  }
+}
+
+// CPUs this process may run on (its affinity mask), else the machine's count.
+int64_t usable_cpus() {
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+    const int n = CPU_COUNT(&set);
+    if (n > 0) return n;
+  }
+  return std::max(1u, std::thread::hardware_concurrency());
+}
+
+int cpu_adamw(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t n_state, int64_t begin, int64_t count,
+              const zero_adamw_hparams* hp, const double* h_rank_sqnorms, int32_t n_ranks, int32_t n_threads,
+              const char* who) {
+  if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
+  if (n_state < 0 || begin < 0 || count < 0 || begin > n_state || count > n_state - begin)
+    return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside a state of %lld elements", who, (long long)begin,
+                (long long)count, (long long)n_state);
+  if (hp->step < 1) return fail(ZERO_EINVAL, "%s: step must be >= 1 (got %lld)", who, (long long)hp->step);
+  const bool clip = hp->max_norm > 0.0;
+  if (clip && (h_rank_sqnorms == nullptr || n_ranks < 1))
+    return fail(ZERO_EINVAL, "%s: clipping needs the ranks' sums of squares", who);
+  if (n_threads < 0) return fail(ZERO_EINVAL, "%s: n_threads < 0", who);
+  if (count == 0) return zero::ok();
+  if (!h_grad || !h_state || !h_param) return fail(ZERO_EINVAL, "%s: NULL buffer", who);
+
+  HostAdam a{};
+  a.beta1 = float(hp->beta1);
+  a.omb1 = float(1.0 - hp->beta1);
+  a.beta2 = float(hp->beta2);
+  a.omb2 = float(1.0 - hp->beta2);
+  const double t = double(hp->step);
+  a.lr_wd = float(hp->lr * hp->weight_decay);
+  a.step_size = float(hp->lr / (1.0 - std::pow(hp->beta1, t)));
+  a.inv_sqrt_bc2 = float(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
+  a.eps = float(hp->eps);
+  a.coef = 1.0f;
+  if (clip) {
+    double G2 = 0.0;
+    for (int32_t r = 0; r < n_ranks; ++r) G2 += h_rank_sqnorms[r];
+    const double ratio = hp->max_norm / (std::sqrt(G2) + hp->clip_eps);
+    a.coef = float(ratio >= 1.0 ? 1.0 : ratio);   // a NaN ratio stays NaN
+  }
+
+  int64_t threads = n_threads > 0 ? n_threads : usable_cpus();
+  const int64_t min_per_thread = 1 << 16;
+  threads = std::max<int64_t>(1, std::min(threads, (count + min_per_thread - 1) / min_per_thread));
+  const int64_t end = begin + count;
+  if (threads == 1) {
+    adam_range(a, h_grad, h_state, h_param, n_state, begin, begin, end);
+    return zero::ok();
+  }
+  // split on 64-element boundaries so no two threads share a cache line
+  const int64_t per = ((count + threads - 1) / threads + 63) / 64 * 64;
+  std::vector<std::thread> pool;
+  try {
+    for (int64_t i = 0; i < threads; ++i) {
+      const int64_t lo = begin + i * per;
+      const int64_t hi = std::min(end, lo + per);
+      if (lo >= hi) break;
+      pool.emplace_back(adam_range, std::cref(a), h_grad, h_state, h_param, n_state, begin, lo, hi);
+    }
+  } catch (...) {
+    for (auto& th : pool) th.join();
+    return fail(ZERO_ENOMEM, "%s: could not start host threads", who);
+  }
+  for (auto& th : pool) th.join();
+  return zero::ok();
+}
+
+}  // namespace
+
+extern "C" int zero_cpu_adamw_step(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t n_state,
+                                   int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                                   const double* h_rank_sqnorms, int32_t n_ranks, int32_t n_threads) {
+  return cpu_adamw(h_grad, h_state, h_param, n_state, begin, count, hp, h_rank_sqnorms, n_ranks, n_threads,
+                   "zero_cpu_adamw_step");
+}

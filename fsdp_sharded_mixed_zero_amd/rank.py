@@ -207,3 +207,102 @@ class RankShard:
         else:
             out.update(pack=pack, sqnorm=2 * self.shard)
         return out
+
+
+class OffloadRank(RankShard):
+    """ZeRO-Offload (the mlqm.cn article's ZeRO-Offload section): the fp32
+    optimizer state lives in host memory and the host cores run AdamW; the GPU
+    keeps the bf16 gradient and parameter shards and runs pack + norm and
+    unpack. Per bucket, the gradient slice goes device->host into a pinned
+    staging slot, the host updates it (zero_cpu_adamw_step), and the bf16
+    parameters come back host->device before the GPU unpacks them. A ring of
+    ``slots`` staging buffers and two copy streams let the PCIe copies of one
+    bucket overlap the host update of another. Shards without buckets are
+    split into pieces of ``bucket`` elements for this overlap."""
+
+    def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda", fill: bool = True,
+                 bucket: int = 1 << 24, slots: int = 3, threads: int | None = None):
+        import numpy as np
+        import os
+
+        super().__init__(wl, rank, device, fill=fill, bucket=wl.bucket or bucket, fused_norm=True)
+        S = self.shard
+        self.h_state = np.empty(3 * S, np.float32)
+        if fill:
+            self.move_state_to_host()
+        self.threads = threads if threads is not None else int(
+            os.environ.get("ZERO_CPU_THREADS", os.environ.get("OMP_NUM_THREADS", "0")) or 0)
+        piece = max(n for _, n in self.pieces())
+        self.stage_g = [torch.empty(piece, dtype=torch.int16, pin_memory=True) for _ in range(slots)]
+        self.stage_p = [torch.empty(piece, dtype=torch.int16, pin_memory=True) for _ in range(slots)]
+        self.h_rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, pin_memory=True)
+        self.d2h = torch.cuda.Stream(device=self.device)
+        self.h2d = torch.cuda.Stream(device=self.device)
+        self.host_seconds = 0.0
+
+    def move_state_to_host(self, piece=1 << 26):
+        """Copy the device state (drawn by fill_state) into host memory and
+        free it on the device: from here on the GPU holds no optimizer state.
+        With fill=False, call fill_state() and then this."""
+        for lo in range(0, 3 * self.shard, piece):
+            hi = min(3 * self.shard, lo + piece)
+            self.h_state[lo:hi] = self.state[lo:hi].cpu().numpy()
+        self.state = None
+        torch.cuda.empty_cache()
+
+    def step(self, step, stream=None, timing=None, events=None, before_micro=None, phases=None):
+        import time
+
+        hp = self.hparams(step)
+        cs = torch.cuda.current_stream()
+        stream = cs.cuda_stream
+        pieces = self.pieces()
+        own = self.rank_sq[self.rank:self.rank + 1]
+        for k, (b, n) in enumerate(pieces):
+            zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, b, n, own, k > 0,
+                                        self.workspace, stream=stream)
+        packed = torch.cuda.Event()
+        packed.record(cs)
+        self.d2h.wait_event(packed)
+        with torch.cuda.stream(self.d2h):
+            self.h_rank_sq.copy_(self.rank_sq, non_blocking=True)
+        sums_ready = torch.cuda.Event()
+        sums_ready.record(self.d2h)
+
+        R = len(self.stage_g)
+        got, sent = [None] * len(pieces), [None] * len(pieces)
+
+        def fetch(i):
+            b, n = pieces[i]
+            with torch.cuda.stream(self.d2h):
+                self.stage_g[i % R][:n].copy_(self.grad_shard[b:b + n].view(torch.int16), non_blocking=True)
+            got[i] = torch.cuda.Event()
+            got[i].record(self.d2h)
+
+        for i in range(min(R, len(pieces))):
+            fetch(i)
+        sums_ready.synchronize()
+        for i, (b, n) in enumerate(pieces):
+            slot = i % R
+            got[i].synchronize()
+            if i >= R:
+                sent[i - R].synchronize()      # the staging slot's previous copy has left
+            t0 = time.perf_counter()
+            zero.zero_cpu_adamw_step(self.stage_g[slot], self.h_state, self.stage_p[slot], self.shard, b, n,
+                                     hp, self.h_rank_sq, self.wl.n_d, self.threads)
+            self.host_seconds += time.perf_counter() - t0
+            with torch.cuda.stream(self.h2d):
+                self.param_shard[b:b + n].view(torch.int16).copy_(self.stage_p[slot][:n], non_blocking=True)
+            sent[i] = torch.cuda.Event()
+            sent[i].record(self.h2d)
+            cs.wait_event(sent[i])
+            zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs, b, n, stream)
+            if i + R < len(pieces):
+                fetch(i + R)
+        for ev in sent[-R:]:
+            ev.synchronize()                   # staging slots free for the next step
+
+    def pcie_bytes_per_step(self):
+        """Bytes the step moves over PCIe: the bf16 gradients down, the bf16
+        parameters up, the partial sums."""
+        return 2 * self.shard + 2 * self.shard + 8 * self.wl.n_d

@@ -81,6 +81,8 @@ _SIGNATURES = {
     "zero_adamw_step_f32grad": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                                ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
     "zero_accumulate_grads": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
+    "zero_cpu_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
+                                           ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _I32]),
     "zero_shard_sqnorm_f32": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_state_import": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
     "zero_state_export": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP]),
@@ -258,6 +260,23 @@ def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count:
     _check("zero_adamw_step_f32grad", library().zero_adamw_step_f32grad(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def _host_ptr(x):
+    """Address of a host buffer: a CPU torch tensor, a numpy array or an int."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def zero_cpu_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
+                        rank_sqnorms, n_ranks: int, n_threads: int = 0):
+    """Host memory throughout (numpy arrays or CPU tensors)."""
+    _check("zero_cpu_adamw_step", library().zero_cpu_adamw_step(
+        _host_ptr(grad), _host_ptr(state), _host_ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _host_ptr(rank_sqnorms), n_ranks, n_threads))
 
 
 def zero_accumulate_grads(grad, acc, count: int, first: bool, stream=None):

@@ -297,6 +297,28 @@ int zero_adamw_step_f32grad(const float* d_grad, float* d_state, uint16_t* d_par
 int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* const* tensor_params,
                        int64_t begin, int64_t count, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * zero_cpu_adamw_step -- ZeRO-Offload: the same update as zero_adamw_step run
+ * by the host cores on HOST memory (the mlqm.cn article's ZeRO-Offload
+ * section: optimizer state in CPU memory, the CPU runs Adam, results return
+ * over PCIe; "別再複製本可分片的東西": CPU offload of the sharded state).
+ * Same update, state layout and arithmetic as zero_adamw_step (fp32 with fused
+ * multiply-adds, correctly rounded sqrt and division, round-to-nearest-even
+ * bf16), so on hosts with hardware FMA it matches the GPU bit for bit.
+ *   h_grad    HOST array of the count bf16 gradients of the range (element
+ *             begin first): a staging buffer the caller fills from the GPU
+ *   h_state   HOST pointer to the tiled fp32 state of all n_state elements
+ *   h_param   HOST array receiving the count bf16 parameters of the range
+ *   h_rank_sqnorms  HOST array of n_ranks doubles
+ *   n_threads host threads to use (0 = all the process may run on)
+ * Pinned staging buffers let the caller overlap the PCIe copies of one range
+ * with the update of another.
+ * Synchronous: returns when the range is updated. Errors: as zero_adamw_step,
+ * plus ZERO_EINVAL for n_threads < 0 and ZERO_ENOMEM if threads cannot start. */
+int zero_cpu_adamw_step(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t n_state,
+                        int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                        const double* h_rank_sqnorms, int32_t n_ranks, int32_t n_threads);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* zero_last_error(void);
 

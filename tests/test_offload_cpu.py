@@ -1,0 +1,91 @@
+"""ZeRO-Offload's host AdamW (zero_cpu_adamw_step) against the oracle, on the
+host: ragged sizes, sub-ranges across tiles and the compact last tile, several
+steps and hyperparameters, thread counts. Needs the library, not a GPU."""
+
+import os
+
+import numpy as np
+import pytest
+
+from fsdp_sharded_mixed_zero_amd import synth, zero
+from oracle import step as O
+from state_tiles import TILE, from_tiles, to_tiles
+from tolerance import assert_bf16_param, assert_f32_state
+
+pytestmark = pytest.mark.skipif(not os.path.exists(zero.LIB_PATH), reason="libzero_mi355x.so not built")
+
+
+def _hp(ohp, step):
+    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
+                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm, clip_eps=ohp.clip_eps,
+                        step=step)
+
+
+def _case(n, begin, count, step, ohp, n_ranks, threads, seed):
+    rng = np.random.default_rng(seed)
+    bits = synth.to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32)
+    parts = np.abs(rng.standard_normal(n_ranks)) * 3e-4 * max(n, 1)
+    state = to_tiles(master, m, v)
+    param = np.full(n, synth.SENTINEL, np.uint16)
+    sl = slice(begin, begin + count)
+    staged = np.full(count, synth.SENTINEL, np.uint16)          # the range only, like a staging buffer
+    zero.zero_cpu_adamw_step(bits[sl].copy(), state, staged, n, begin, count, _hp(ohp, step), parts, n_ranks,
+                             threads)
+    param[sl] = staged
+    coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
+    want = O.adamw_step(bits[sl], master[sl], m[sl], v[sl], step, ohp, coef)
+    g_master, g_m, g_v = from_tiles(state, n)
+    out = np.ones(n, bool)
+    out[sl] = False
+    assert np.array_equal(g_master[out], master[out]) and np.array_equal(g_v[out], v[out])
+    assert (param[out] == synth.SENTINEL).all()
+    assert_f32_state(g_master[sl], want[0], "master")
+    assert_f32_state(g_m[sl], want[1], "m", m[sl])
+    assert_f32_state(g_v[sl], want[2], "v", v[sl])
+    assert_bf16_param(param[sl], want[3], want[0], "param", g_master[sl])
+    return state, param
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, TILE - 1, TILE + 5, 3 * TILE + 6, 300_001])
+def test_cpu_adamw_whole(n):
+    _case(n, 0, n, 3, O.AdamWHParams(), 4, 4, seed=n)
+
+
+@pytest.mark.parametrize("begin,count", [(1, 2), (5, TILE), (TILE - 2, 9), (4, 3 * TILE), (2 * TILE + 1, 3),
+                                         (7, 0)])
+def test_cpu_adamw_sub_ranges(begin, count):
+    _case(3 * TILE + 10, begin, count, 2, O.AdamWHParams(), 2, 3, seed=begin + 17 * count)
+
+
+@pytest.mark.parametrize("step", [1, 1000])
+def test_cpu_adamw_hyperparameters(step):
+    for ohp in (O.AdamWHParams(max_norm=0.0),
+                O.AdamWHParams(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1, max_norm=0.05)):
+        _case(50_000, 0, 50_000, step, ohp, 8, 2, seed=step)
+
+
+def test_cpu_adamw_threads_agree():
+    # the split across threads does not change any bit
+    outs = [_case(1_000_003, 0, 1_000_003, 5, O.AdamWHParams(), 4, t, seed=5) for t in (1, 3, 8, 0)]
+    for state, param in outs[1:]:
+        assert np.array_equal(state.view(np.uint32), outs[0][0].view(np.uint32))
+        assert np.array_equal(param, outs[0][1])
+
+
+def test_cpu_adamw_rejects_bad_arguments():
+    hp = zero.hparams(step=1)
+    x = np.zeros(8, np.float32)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 4, 5, hp,
+                                 np.ones(1), 1)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 0, 8, hp, None, 0)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 0, 8, hp,
+                                 np.ones(1), 1, -2)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 0, 8,
+                                 zero.hparams(step=0), np.ones(1), 1)
