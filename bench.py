@@ -38,10 +38,16 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the plain-copy ceiling (it launches the unpack kernel, so profiled runs "
+                         "leave it out to keep that kernel's statistics to the step's own launches)")
     ap.add_argument("--separate-norm", action="store_true",
                     help="run pack and the sum of squares as two calls instead of the fused one")
     ap.add_argument("--accum", type=int, default=1, metavar="K",
                     help="fp32 gradient accumulation over K micro-batches per step (K > 1)")
+    ap.add_argument("--flat", action="store_true",
+                    help="ZeRO-1 flat buffers: gradients and parameters are views into flat buffers, the "
+                         "shard is the rank's slice (no pack, no unpack)")
     ap.add_argument("--offload", action="store_true",
                     help="ZeRO-Offload: fp32 state in host memory, AdamW on the host cores")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -64,15 +70,17 @@ def kernel_name(raw):
     return name.split("(")[0].split("::")[-1]
 
 
-def algorithmic_bytes(wl, accum=1, separate_norm=False):
+def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False):
     """Algorithmic HBM bytes per step of each kernel over the whole shard, for
-    the benchmark's mode (fused norm by default, separate norm, or fp32
-    accumulation over ``accum`` micro-batches)."""
+    the benchmark's mode (fused norm by default, separate norm, fp32
+    accumulation over ``accum`` micro-batches, or flat buffers)."""
     from fsdp_sharded_mixed_zero_amd import zero
     info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
     S = info["shard"]
     real = S - (info["pad_end"] - info["pad_begin"])
     pack = 4 * real + 2 * (S - real)
+    if flat:
+        return S, real, {"sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel<unsigned short>": 28 * S}
     out = {"copy_pieces_kernel<false>": 4 * real}          # unpack
     if accum > 1:
         out["copy_pieces_kernel<false>"] += accum * pack   # plus one pack per micro-batch
@@ -145,9 +153,9 @@ def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline",
+                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline --no-copy-ceiling",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline",
+                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline --no-copy-ceiling",
                 f"python bench.py --workload {wl.name} --steps 20 --warmup 2 "
                 f"--pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
@@ -158,7 +166,7 @@ def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
             "kernels": kernels}
 
 
-def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False):
+def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False):
     """Markdown table of a rocprofv3 kernel-stats CSV of this benchmark, with
     achieved bandwidth from each kernel's algorithmic bytes per launch (the
     step's bytes spread over that kernel's launches per step)."""
@@ -166,15 +174,17 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False):
     import glob
 
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
-    S, real, algo = algorithmic_bytes(wl, accum, separate_norm)
+    S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat)
     rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
     steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S)
-    mode = (f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "")
+    mode = ((f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "") +
+            (" --flat" if flat else ""))
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
              f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
              "Command (repository root, one MI355X):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o bench -- "
-             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} --no-cpu-baseline",
+             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
+             f"--no-cpu-baseline --no-copy-ceiling",
              f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
              f"--stats-summary {stats_dir}", "",
              f"kernels.hip sha256: `{source_hash()}`", "",
@@ -212,66 +222,167 @@ def measured_traffic(workload, kernel):
 
 # --------------------------------------------------------------- oracle leg
 
+ORACLE_CHUNK = 1 << 22
+
+
+def _oracle_setup(wl):
+    """The rank's layout, hyperparameters, the other ranks' expected sum of
+    squares, and the number of 2^22-element chunks of the shard."""
+    from oracle import step as O
+    from oracle.layout import build_layout
+
+    lay = build_layout(wl.sizes, wl.n_d, wl.rank, wl.align)
+    hp = O.AdamWHParams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                        weight_decay=wl.weight_decay, max_norm=wl.max_norm)
+    others = sum(max(0, min(lay.shard, lay.psi - r * lay.shard)) for r in range(wl.n_d)
+                 if r != wl.rank) * wl.grad_sq_mean()
+    return lay, hp, others, max(1, lay.shard // ORACLE_CHUNK)
+
+
+def _oracle_sample(wl, lay, k, n_chunks):
+    """Chunk k of the shard (spread across it) as its own small layout over
+    windows of the tensors it covers, with its gradients and state."""
+    from fsdp_sharded_mixed_zero_amd import synth
+    from oracle.layout import Layout, Segment
+
+    b = (k * 7919 % n_chunks) * ORACLE_CHUNK
+    c = min(ORACLE_CHUNK, lay.shard - b)
+    segs, wins = [], []
+    for s in lay.segments:
+        lo, hi = max(s.dst_off, b), min(s.dst_off + s.length, b + c)
+        if lo < hi:
+            segs.append(Segment(len(wins), 0, lo - b, hi - lo))
+            wins.append(hi - lo)
+    sub = Layout(tuple(wins), 1, 0, 1, (), lay.psi, c, c, 0, tuple(segs), c, c)
+    grads = [synth.to_bf16_bits(synth.host_grad_f32(n, wl, wl.step, 1000 + i)) for i, n in enumerate(wins)]
+    real = max(0, min(c, lay.real_elems - b))
+    return b, c, sub, grads, synth.host_shard_state(wl, b, c, real, piece=k)
+
+
+def _oracle_run(wl, hp, others, sample):
+    """One oracle step over a sample; returns the seconds it took."""
+    import numpy as np
+
+    from oracle import step as O
+
+    _, _, sub, grads, (master, m, v) = sample
+    params = [np.zeros(n, np.uint16) for n in sub.sizes]
+    t0 = time.perf_counter()
+    g = O.pack(sub, grads)
+    G = O.global_sqnorm([O.sqnorm(g), others])
+    coef = O.clip_coef(G, hp.max_norm, hp.clip_eps)
+    _, _, _, bits = O.adamw_step(g, master, m, v, wl.step, hp, coef)
+    O.unpack(sub, bits, params)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(wl, seconds):
     """The oracle's step (pack, sum of squares, clip, AdamW, unpack) on chunks
     of 2^22 shard elements taken from across the rank's shard, on one host
     thread, repeated over up to 8 distinct chunks until about ``seconds`` of
     oracle time has been spent (input generation is not timed)."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from fsdp_sharded_mixed_zero_amd import synth
-    from oracle import step as O
-    from oracle.layout import Layout, Segment, build_layout
-
-    lay = build_layout(wl.sizes, wl.n_d, wl.rank, wl.align)
-    chunk = 1 << 22
-    n_chunks = max(1, lay.shard // chunk)
-    hp = O.AdamWHParams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
-                        weight_decay=wl.weight_decay, max_norm=wl.max_norm)
-    others = sum(max(0, min(lay.shard, lay.psi - r * lay.shard)) for r in range(wl.n_d)
-                 if r != wl.rank) * wl.grad_sq_mean()
-    samples = []
-    for k in range(min(8, n_chunks)):
-        b = (k * 7919 % n_chunks) * chunk
-        c = min(chunk, lay.shard - b)
-        # the chunk as its own small layout over windows of the tensors it covers
-        segs, wins = [], []
-        for s in lay.segments:
-            lo, hi = max(s.dst_off, b), min(s.dst_off + s.length, b + c)
-            if lo < hi:
-                segs.append(Segment(len(wins), 0, lo - b, hi - lo))
-                wins.append(hi - lo)
-        sub = Layout(tuple(wins), 1, 0, 1, (), lay.psi, c, c, 0, tuple(segs), c, c)
-        grads = [synth.to_bf16_bits(synth.host_grad_f32(n, wl, wl.step, 1000 + i))
-                 for i, n in enumerate(wins)]
-        real = max(0, min(c, lay.real_elems - b))
-        samples.append((b, c, sub, grads, synth.host_shard_state(wl, b, c, real, piece=k)))
-    def run(sample):
-        _, _, sub, grads, (master, m, v) = sample
-        params = [np.zeros(n, np.uint16) for n in sub.sizes]
-        t0 = time.perf_counter()
-        g = O.pack(sub, grads)
-        G = O.global_sqnorm([O.sqnorm(g), others])
-        coef = O.clip_coef(G, hp.max_norm, hp.clip_eps)
-        _, _, _, bits = O.adamw_step(g, master, m, v, wl.step, hp, coef)
-        O.unpack(sub, bits, params)
-        return time.perf_counter() - t0
-
+    lay, hp, others, n_chunks = _oracle_setup(wl)
+    samples = [_oracle_sample(wl, lay, k, n_chunks) for k in range(min(8, n_chunks))]
     done = 0
     spent = 0.0
     runs = 0
     with threadpool_limits(limits=1):
-        run(samples[0])        # untimed: the first call pays one-time start-up costs
+        _oracle_run(wl, hp, others, samples[0])    # untimed: the first call pays start-up costs
         while spent < seconds:
             sample = samples[runs % len(samples)]
-            spent += run(sample)
+            spent += _oracle_run(wl, hp, others, sample)
             done += sample[1]
             runs += 1
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{runs} runs over {len(samples)} distinct chunks of {chunk} elements of the "
+            "sample": (f"{runs} runs over {len(samples)} distinct chunks of {ORACLE_CHUNK} elements of the "
                        f"{wl.name} rank-{wl.rank} shard ({done} elements, {spent:.1f} s of oracle time), "
                        f"numpy float64 oracle on one host thread")}
+
+
+def _oracle_worker(name, k, seconds, barrier, results):
+    """One process of the parallel baseline: its own chunk, one thread, timed
+    from a barrier that all workers pass together."""
+    from threadpoolctl import threadpool_limits
+
+    from fsdp_sharded_mixed_zero_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    lay, hp, others, n_chunks = _oracle_setup(wl)
+    sample = _oracle_sample(wl, lay, k % n_chunks, n_chunks)
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        _oracle_run(wl, hp, others, sample)
+        barrier.wait()
+        while spent < seconds:
+            spent += _oracle_run(wl, hp, others, sample)
+            done += sample[1]
+    results.put((done, spent))
+
+
+def cpu_baseline_parallel(wl, seconds, workers):
+    """The same oracle step in ``workers`` single-threaded processes at once,
+    each on its own chunk (the bucket-parallel form: chunks are independent
+    once the clip coefficient is known). Throughput = the sum of the workers'
+    rates over the common timed window."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")          # fresh interpreters: nothing inherited from the GPU process
+    barrier = ctx.Barrier(workers)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(wl.name, k, seconds, barrier, results))
+             for k in range(workers)]
+    for pr in procs:
+        pr.start()
+    out = [results.get(timeout=600) for _ in procs]
+    for pr in procs:
+        pr.join()
+    rate = sum(d / s for d, s in out)
+    return {"value": rate, "unit": "params/s", "cores": workers, "kind": "oracle",
+            "sample": (f"{workers} processes, one host thread each, each on its own chunk of {ORACLE_CHUNK} "
+                       f"elements of the {wl.name} rank-{wl.rank} shard for about {seconds:.0f} s "
+                       f"({sum(d for d, _ in out)} elements in all)")}
+
+
+def copy_ceiling(torch, nbytes, reps=20):
+    """The streaming ceiling the kernels are compared with: a plain copy that
+    moves ``nbytes`` per launch (half read, half written), timed with HIP
+    events around each launch like the kernels. The copy is the library's
+    unpack over a one-tensor layout (one piece: the plain copy kernel);
+    torch's device-to-device ``copy_`` of the same bytes is listed beside it."""
+    from fsdp_sharded_mixed_zero_amd import zero
+
+    n = max(8, nbytes // 4 // 8 * 8)       # bf16 elements; the copy moves 4 bytes each
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    lay = zero.zero_layout([n], 1, 0, 1)
+    ptrs = zero.pointer_array([dst])
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def per_launch(fn):
+        for _ in range(3):
+            fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for e0, e1 in pairs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e-3 / reps
+
+    sec = per_launch(lambda: zero.zero_unpack_params(lay, src, ptrs, 0, n, stream))
+    ok = torch.equal(dst.view(torch.int16), src.view(torch.int16))
+    sec_torch = per_launch(lambda: dst.copy_(src))
+    gbps, gbps_torch = 4 * n / sec / 1e9, 4 * n / sec_torch / 1e9
+    del src, dst, lay
+    torch.cuda.empty_cache()
+    return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_copy": 4 * n,
+            "copied_correctly": ok,
+            "how": f"zero_unpack_params over a one-tensor layout of {n} bf16 elements, mean of {reps} "
+                   f"launches with events around each",
+            "torch_copy_GBps": round(gbps_torch, 1)}
 
 
 # ------------------------------------------------------------------ GPU leg
@@ -328,7 +439,7 @@ def main():
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth
         print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup,
-                            args.accum, args.separate_norm), end="")
+                            args.accum, args.separate_norm, args.flat), end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -343,11 +454,19 @@ def main():
     from fsdp_sharded_mixed_zero_amd.rank import RankShard
 
     zero.library()                       # fail loudly if the HIP library is missing
-    torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
+    # the oracle legs run first, before this process touches the GPU, so the
+    # parallel leg starts its worker processes from a process with no GPU state
+    baselines = {}
+    if not args.no_cpu_baseline and not args.offload:
+        baselines["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        workers = min(16, len(os.sched_getaffinity(0)))
+        if workers > 1:
+            baselines["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, args.cpu_seconds / 3, workers)
+    torch.cuda.set_device(0)
     if args.offload:
         return offload_main(args, wl)
-    rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum)
+    rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum, flat=args.flat)
     torch.cuda.synchronize()
 
     t = wl.step
@@ -410,11 +529,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} rank {rs.rank} of N_d={wl.n_d}: one rank's shard, "
-                               f"pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack",
+        "config": {"workload": f"{wl.name} rank {rs.rank} of N_d={wl.n_d}: one rank's shard, " + (
+                               "ZeRO-1 flat buffers: sum of squares -> clip+AdamW+bf16 cast on the rank's slice"
+                               if args.flat else "pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack"),
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
                    "segments_in_shard": len(rs.segments), "adamw_step": wl.step,
-                   "bucket": rs.bucket, "norm": "separate" if args.separate_norm else "fused into pack",
+                   "bucket": rs.bucket,
+                   "norm": "separate" if args.separate_norm or args.flat else "fused into pack",
                    "fp32_grad_accumulation_micro_batches": args.accum if args.accum > 1 else None},
         "adamw_params_per_s": launch_elems / (adamw_launch_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -427,8 +548,9 @@ def main():
     }
     del rs
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if not args.no_copy_ceiling:
+        out["copy_ceiling"] = copy_ceiling(torch, min(int(launch_bytes), 8 << 30))
+    out.update(baselines)
     print(json.dumps(out), flush=True)
 
 
