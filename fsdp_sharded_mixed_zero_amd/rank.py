@@ -19,6 +19,13 @@ working set (notes, section 5.2). With ``accum_steps`` = K > 1 the step runs
 K micro-batches of pack + fp32 accumulation, then the norm and AdamW on the
 fp32 accumulator ("第 5 课：ZeRO 与 FSDP" section 2, fp32 gradient
 accumulation, 4 extra bytes per shard element).
+
+With ``flat=True`` the rank holds the ZeRO-1 form (notes on the ZeRO paper,
+section 4.1): the whole gradient and parameter sets live in two flat,
+padded buffers, every tensor is a view into them, and the shard is the rank's
+slice of each. The step then reads the gradient slice in place (no pack) and
+AdamW writes the bf16 parameters straight into the flat parameter buffer (no
+unpack): sum of squares -> clip + AdamW + bf16 cast.
 """
 
 from __future__ import annotations
@@ -31,7 +38,7 @@ from . import synth, zero
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
                  fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
-                 accum_steps: int = 1):
+                 accum_steps: int = 1, flat: bool = False):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -47,14 +54,32 @@ class RankShard:
         self.grads = [None] * n_t
         self.params = [None] * n_t
         dev = self.device
-        for i in self.touched:
-            self.grads[i] = torch.empty(wl.sizes[i], dtype=torch.bfloat16, device=dev)
-            self.params[i] = torch.full((wl.sizes[i],), synth.SENTINEL, dtype=torch.int16,
-                                        device=dev).view(torch.bfloat16)
+        self.flat = flat
+        if flat:
+            if accum_steps > 1:
+                raise ValueError("flat buffers are not combined with gradient accumulation here")
+            P, lo = self.info["padded"], self.info["shard_begin"]
+            self.grad_flat = torch.empty(P, dtype=torch.bfloat16, device=dev)
+            self.grad_flat[self.info["psi"]:].zero_()          # padding reads as zero gradients
+            self.param_flat = torch.full((P,), synth.SENTINEL, dtype=torch.int16,
+                                         device=dev).view(torch.bfloat16)
+            off = 0
+            for i, n in enumerate(wl.sizes):
+                if i in self.touched:
+                    self.grads[i] = self.grad_flat[off:off + n]
+                    self.params[i] = self.param_flat[off:off + n]
+                off += n
+            self.grad_shard = self.grad_flat[lo:lo + S]
+            self.param_shard = self.param_flat[lo:lo + S]
+        else:
+            for i in self.touched:
+                self.grads[i] = torch.empty(wl.sizes[i], dtype=torch.bfloat16, device=dev)
+                self.params[i] = torch.full((wl.sizes[i],), synth.SENTINEL, dtype=torch.int16,
+                                            device=dev).view(torch.bfloat16)
+            self.grad_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
+            self.param_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
         self.grad_ptrs = zero.pointer_array(self.grads)
         self.param_ptrs = zero.pointer_array(self.params)
-        self.grad_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
-        self.param_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
         self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
         self.fused_norm = fused_norm
@@ -152,6 +177,9 @@ class RankShard:
         if self.accum_steps > 1:
             self._step_accumulated(hp, own, pieces, stream, mark, before_micro)
             return
+        if self.flat:
+            self._step_flat(hp, own, pieces, stream, mark)
+            return
         for k, (b, n) in enumerate(pieces):
             if self.fused_norm:
                 mark("pack_sqnorm", lambda: zero.zero_pack_grads_sqnorm(
@@ -168,6 +196,15 @@ class RankShard:
                 self.wl.n_d, stream))
             mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
+
+    def _step_flat(self, hp, own, pieces, stream, mark):
+        for k, (b, n) in enumerate(pieces):
+            mark("sqnorm", lambda: zero.zero_shard_sqnorm(self.grad_shard[b:], n, own, k > 0, self.workspace,
+                                                          stream=stream))
+        for b, n in pieces:
+            mark("adamw", lambda: zero.zero_adamw_step(
+                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                self.wl.n_d, stream))
 
     def _step_accumulated(self, hp, own, pieces, stream, mark, before_micro):
         for mb in range(self.accum_steps):
@@ -193,7 +230,10 @@ class RankShard:
         fused into pack), AdamW 28 and unpack 4 bytes per shard element (pack
         writes only 2 on padding, unpack moves nothing there). Accumulating K
         micro-batches: K packs, accumulation 6 then 10 bytes per element, an
-        fp32 norm (4) and AdamW on fp32 gradients (30)."""
+        fp32 norm (4) and AdamW on fp32 gradients (30). Flat buffers: the sum
+        of squares (2) and AdamW (28) only."""
+        if self.flat:
+            return {"sqnorm": 2 * self.shard, "adamw": 28 * self.shard}
         pad = self.shard - self.real
         pack = 4 * self.real + 2 * pad
         if self.accum_steps > 1:
