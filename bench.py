@@ -50,6 +50,9 @@ def parse():
                          "shard is the rank's slice (no pack, no unpack)")
     ap.add_argument("--offload", action="store_true",
                     help="ZeRO-Offload: fp32 state in host memory, AdamW on the host cores")
+    ap.add_argument("--offload-bucket", type=int, default=1 << 24, metavar="N",
+                    help="elements per PCIe staging bucket in the offload step (workloads with their "
+                         "own bucket size keep it)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into HBM bytes per launch and exit")
@@ -394,7 +397,7 @@ def offload_main(args, wl):
 
     from fsdp_sharded_mixed_zero_amd.rank import OffloadRank
 
-    rs = OffloadRank(wl)
+    rs = OffloadRank(wl, bucket=args.offload_bucket)
     torch.cuda.synchronize()
     t = wl.step
     for _ in range(args.warmup):

@@ -12,13 +12,20 @@
 // across threads by whole elements ranges; each thread walks the tiles its
 // range meets and runs a contiguous, vectorisable loop per tile. The inner
 // loop is compiled for AVX-512, AVX2+FMA and baseline x86-64 and picked at run
-// time.
+// time. One core streams only ~15 GB/s, so the update needs many cores; the
+// threads are kept in a pool for the life of the process, because a bucketed
+// step makes one call per bucket and starting threads per call costs 10% or
+// more of it.
 #include <sched.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <cmath>
+#include <condition_variable>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -81,6 +88,91 @@ void adam_range(const HostAdam& a, const uint16_t* g, float* state, uint16_t* pa
   }
 }
 
+// Worker threads started on first use and kept until the process ends. run()
+// calls task(i) for i = 0..n-1, task(0) on the calling thread, and returns when
+// all are done. Calls are serialised. All shared state (threads, mutex,
+// condition variables) sits in one heap object: a child made by fork() has
+// none of the parent's threads, and the inherited condition variables still
+// count the parent's waiters, so the child abandons that object (it is never
+// freed or joined) and builds its own. Forking while a call runs is not
+// supported.
+struct PoolState {
+  std::mutex mu;
+  std::condition_variable cv, done;
+  std::vector<std::thread> threads;
+  const std::function<void(int)>* task = nullptr;
+  int n = 0, pending = 0;
+  uint64_t gen = 0;
+  bool stop = false;
+  pid_t owner = getpid();
+};
+
+void pool_loop(PoolState* st, int id) {
+  uint64_t seen = 0;
+  std::unique_lock<std::mutex> lk(st->mu);
+  for (;;) {
+    st->cv.wait(lk, [&] { return st->stop || st->gen != seen; });
+    if (st->stop) return;
+    seen = st->gen;
+    if (id >= st->n) continue;           // this call needs fewer threads
+    const std::function<void(int)>* t = st->task;
+    lk.unlock();
+    (*t)(id);
+    lk.lock();
+    if (--st->pending == 0) st->done.notify_one();
+  }
+}
+
+class WorkerPool {
+ public:
+  ~WorkerPool() {
+    if (st_ == nullptr || st_->owner != getpid()) return;
+    {
+      std::lock_guard<std::mutex> g(st_->mu);
+      st_->stop = true;
+    }
+    st_->cv.notify_all();
+    for (auto& t : st_->threads) t.join();
+    delete st_;
+  }
+
+  // false if threads could not be started (nothing has run then)
+  bool run(int n, const std::function<void(int)>& task) {
+    std::lock_guard<std::mutex> serial(call_mu_);
+    if (st_ == nullptr || st_->owner != getpid()) st_ = new PoolState();
+    PoolState* st = st_;
+    std::unique_lock<std::mutex> lk(st->mu);
+    try {
+      while (int(st->threads.size()) < n - 1) {
+        const int id = int(st->threads.size()) + 1;
+        st->threads.emplace_back(pool_loop, st, id);
+      }
+    } catch (...) {
+      return false;
+    }
+    st->task = &task;
+    st->n = n;
+    st->pending = n - 1;
+    ++st->gen;
+    lk.unlock();
+    st->cv.notify_all();
+    task(0);
+    lk.lock();
+    st->done.wait(lk, [st] { return st->pending == 0; });
+    st->task = nullptr;
+    return true;
+  }
+
+ private:
+  std::mutex call_mu_;
+  PoolState* st_ = nullptr;
+};
+
+WorkerPool& pool() {
+  static WorkerPool p;
+  return p;
+}
+
 // CPUs this process may run on (its affinity mask), else the machine's count.
 int64_t usable_cpus() {
   cpu_set_t set;
@@ -135,19 +227,12 @@ int cpu_adamw(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t
   }
   // split on 64-element boundaries so no two threads share a cache line
   const int64_t per = ((count + threads - 1) / threads + 63) / 64 * 64;
-  std::vector<std::thread> pool;
-  try {
-    for (int64_t i = 0; i < threads; ++i) {
-      const int64_t lo = begin + i * per;
-      const int64_t hi = std::min(end, lo + per);
-      if (lo >= hi) break;
-      pool.emplace_back(adam_range, std::cref(a), h_grad, h_state, h_param, n_state, begin, lo, hi);
-    }
-  } catch (...) {
-    for (auto& th : pool) th.join();
-    return fail(ZERO_ENOMEM, "%s: could not start host threads", who);
-  }
-  for (auto& th : pool) th.join();
+  const int n_run = int((count + per - 1) / per);
+  const std::function<void(int)> task = [&](int i) {
+    const int64_t lo = begin + int64_t(i) * per;
+    adam_range(a, h_grad, h_state, h_param, n_state, begin, lo, std::min(end, lo + per));
+  };
+  if (!pool().run(n_run, task)) return fail(ZERO_ENOMEM, "%s: could not start host threads", who);
   return zero::ok();
 }
 

@@ -310,7 +310,9 @@ int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* c
  *   h_state   HOST pointer to the tiled fp32 state of all n_state elements
  *   h_param   HOST array receiving the count bf16 parameters of the range
  *   h_rank_sqnorms  HOST array of n_ranks doubles
- *   n_threads host threads to use (0 = all the process may run on)
+ *   n_threads host threads to use (0 = all the process may run on); the
+ *             library keeps its threads for the life of the process, and
+ *             concurrent calls run one after another
  * Pinned staging buffers let the caller overlap the PCIe copies of one range
  * with the update of another.
  * Synchronous: returns when the range is updated. Errors: as zero_adamw_step,

@@ -89,3 +89,36 @@ def test_cpu_adamw_rejects_bad_arguments():
     with pytest.raises(zero.ZeroError):
         zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 0, 8,
                                  zero.hparams(step=0), np.ones(1), 1)
+
+
+def test_cpu_adamw_in_forked_child():
+    """The host threads are kept between calls; a child made by fork() has
+    none of them and must still run the update, with the parent's result.
+    The child calls only the library (the inputs are made with numpy in the
+    parent: torch's CPU thread pool does not survive a fork)."""
+    n = 300_000
+    rng = np.random.default_rng(11)
+    bits = ((rng.standard_normal(n).astype(np.float32) * 1e-3).view(np.uint32) >> 16).astype(np.uint16)
+    state0 = to_tiles((rng.standard_normal(n) * 0.02).astype(np.float32),
+                      (rng.standard_normal(n) * 1e-4).astype(np.float32),
+                      np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32))
+    parts = np.array([0.3, 0.5])
+    hp = _hp(O.AdamWHParams(), 4)
+
+    def run():
+        state, param = state0.copy(), np.zeros(n, np.uint16)
+        zero.zero_cpu_adamw_step(bits, state, param, n, 0, n, hp, parts, 2, 4)
+        return state, param
+
+    first = run()
+    pid = os.fork()
+    if pid == 0:
+        code = 1
+        try:
+            again = run()
+            code = 0 if (np.array_equal(again[0].view(np.uint32), first[0].view(np.uint32))
+                         and np.array_equal(again[1], first[1])) else 2
+        finally:
+            os._exit(code)
+    _, status = os.waitpid(pid, 0)
+    assert os.WIFEXITED(status) and os.WEXITSTATUS(status) == 0
