@@ -234,6 +234,40 @@ def test_pack_more_segments_than_one_launch_holds():
         assert np.array_equal(to_host_u16(o), x)
 
 
+@pytest.mark.parametrize("sizes", [[37] * 60 + [3_000_000] + [11] * 3,
+                                   [3_000_000] + [37] * 60 + [11] * 3,
+                                   [2_001] * 30 + [1_500_000] + [3] * 20 + [700_000] + [5] * 12])
+def test_pack_unpack_many_pieces_per_slot(sizes):
+    """Launches of up to 64 pieces where many one-block pieces share a slot of
+    the kernels' piece lookup (several blocks per slot), so a wave steps
+    forward over several pieces; plain copy and copy + sum of squares, on a
+    whole shard and on a range that starts and ends inside pieces."""
+    rng = np.random.default_rng(len(sizes))
+    host = [synth.to_bf16_bits((rng.standard_normal(n) * 1e-2).astype(np.float32)) for n in sizes]
+    dev = [to_dev_u16(x) for x in host]
+    lay = build_layout(sizes, 1, 0, 1)
+    h = zero.zero_layout(sizes, 1, 0, 1)
+    S = lay.shard
+    assert len(lay.segments) == len(sizes) <= 64
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for b, c in ((0, S), (1_000, S - 2_017)):
+        want = O.pack(lay, host, b, c)
+        shard = sentinel(S)
+        zero.zero_pack_grads(h, dev, shard, b, c)
+        assert np.array_equal(to_host_u16(shard)[b:b + c], want)
+        ws = torch.empty(zero.zero_pack_sqnorm_workspace_bytes(h, b, c) // 8, dtype=torch.float64, device=DEV)
+        shard2 = sentinel(S)
+        zero.zero_pack_grads_sqnorm(h, dev, shard2, b, c, out, False, ws)
+        assert np.array_equal(to_host_u16(shard2)[b:b + c], want)
+        total, exact = float(out.cpu()[0]), O.sqnorm(want)
+        assert abs(total - exact) <= 1e-12 * exact
+        outs = [sentinel(n) for n in sizes]
+        zero.zero_unpack_params(h, shard, outs, b, c)
+        ref = O.unpack(lay, want, [np.full(n, synth.SENTINEL, np.uint16) for n in sizes], b, c)
+        for o, r in zip(outs, ref):
+            assert np.array_equal(to_host_u16(o), r)
+
+
 def test_pack_rejects_missing_tensor_pointer():
     sizes = [100, 100]
     h = zero.zero_layout(sizes, 1, 0, 1)
