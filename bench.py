@@ -116,7 +116,7 @@ def traffic_file(workload):
     return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
-def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
+def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, accum=1, separate_norm=False):
     """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for the copy kernel of known size (the plain copy_pieces_kernel: unpack
@@ -135,6 +135,8 @@ def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
 
     fetch, n_f = load(fetch_dir, "FETCH_SIZE")
     write, n_w = load(write_dir, "WRITE_SIZE")
+    mode = (f"--steps {steps} --warmup {warmup}" + (f" --accum {accum}" if accum > 1 else "") +
+            (" --separate-norm" if separate_norm else ""))
     S, real, algo = algorithmic_bytes(wl, accum, separate_norm)
     steps = steps_traced(n_f, wl, S)
     # the plain copy (unpack) reads and writes exactly 2 bytes per real element
@@ -156,11 +158,10 @@ def pmc_summary(fetch_dir, write_dir, wl, accum=1, separate_norm=False):
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline --no-copy-ceiling",
+                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline --no-copy-ceiling",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} --steps 20 --warmup 2 --no-cpu-baseline --no-copy-ceiling",
-                f"python bench.py --workload {wl.name} --steps 20 --warmup 2 "
-                f"--pmc-summary {fetch_dir} {write_dir}"],
+                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline --no-copy-ceiling",
+                f"python bench.py --workload {wl.name} {mode} --pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
             "kernel_source_sha256": source_hash(),
             "calibration": {"kernel": copy, "known_read_kib": known_read,
@@ -436,8 +437,8 @@ def main():
     args = parse()
     if args.pmc_summary:
         from fsdp_sharded_mixed_zero_amd import synth
-        print(json.dumps(pmc_summary(*args.pmc_summary, synth.WORKLOADS[args.workload], args.accum,
-                                     args.separate_norm), indent=1))
+        print(json.dumps(pmc_summary(*args.pmc_summary, synth.WORKLOADS[args.workload], args.steps,
+                                     args.warmup, args.accum, args.separate_norm), indent=1))
         return
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth

@@ -1,0 +1,136 @@
+"""The benchmark's host logic, on the CPU: kernel-name parsing, the
+algorithmic byte counts every bandwidth figure divides by, the rocprofv3
+summaries (kernel statistics and the calibrated HBM byte counters) on
+synthetic CSV files with known answers, and the refusal of more than one
+GPU. The byte counts need the library (for the layout), not a GPU."""
+
+import csv
+import dataclasses
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from fsdp_sharded_mixed_zero_amd import synth, zero  # noqa: E402
+
+needs_lib = pytest.mark.skipif(not os.path.exists(zero.LIB_PATH), reason="libzero_mi355x.so not built")
+
+
+def test_kernel_name():
+    cases = {
+        "void (anonymous namespace)::copy_pieces_kernel<true>((anonymous namespace)::CopyPieces, double*)":
+            "copy_pieces_kernel<true>",
+        "(anonymous namespace)::sqnorm_final_kernel(double const*, long, double*, int)": "sqnorm_final_kernel",
+        "void (anonymous namespace)::adamw_vec_kernel<unsigned short>((anonymous namespace)::AdamWArgs)":
+            "adamw_vec_kernel<unsigned short>",
+        "accumulate_kernel": "accumulate_kernel",
+    }
+    for raw, short in cases.items():
+        assert bench.kernel_name(raw) == short
+
+
+@needs_lib
+def test_algorithmic_bytes_modes():
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    s, real, b = bench.algorithmic_bytes(wl)
+    assert (s, real) == (S, S)
+    assert b == {"copy_pieces_kernel<false>": 4 * S, "copy_pieces_kernel<true>": 4 * S,
+                 "adamw_vec_kernel<unsigned short>": 28 * S}
+    _, _, b = bench.algorithmic_bytes(wl, separate_norm=True)
+    assert b == {"copy_pieces_kernel<false>": 8 * S, "sqnorm_partial_kernel": 2 * S,
+                 "adamw_vec_kernel<unsigned short>": 28 * S}
+    _, _, b = bench.algorithmic_bytes(wl, accum=4)
+    assert b == {"copy_pieces_kernel<false>": 4 * S + 4 * 4 * S, "accumulate_kernel": (6 + 30) * S,
+                 "sqnorm_f32_partial_kernel": 4 * S, "adamw_vec_kernel<float>": 30 * S}
+    _, _, b = bench.algorithmic_bytes(wl, flat=True)
+    assert b == {"sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel<unsigned short>": 28 * S}
+
+
+@needs_lib
+def test_algorithmic_bytes_with_padding():
+    # GPT-2 1.5B's last rank holds 7,488 padding elements: pack writes 2 bytes
+    # there and reads nothing, unpack moves nothing
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2-1.5b"], rank=63)
+    S, real, b = bench.algorithmic_bytes(wl)
+    assert S - real == 7_488
+    assert b["copy_pieces_kernel<true>"] == 4 * real + 2 * (S - real)
+    assert b["copy_pieces_kernel<false>"] == 4 * real
+    assert b["adamw_vec_kernel<unsigned short>"] == 28 * S
+
+
+def _write_csv(path, fields, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+@needs_lib
+def test_stats_summary_table(tmp_path):
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    ns = "(anonymous namespace)::"
+    names = {"adamw": f"void {ns}adamw_vec_kernel<unsigned short>({ns}AdamWArgs)",
+             "pack": f"void {ns}copy_pieces_kernel<true>({ns}CopyPieces, double*)",
+             "unpack": f"void {ns}copy_pieces_kernel<false>({ns}CopyPieces, double*)",
+             "final": f"{ns}sqnorm_final_kernel(double const*, long, double*, int)"}
+    # 12 steps traced; AdamW 2 us per launch, pack and unpack 1 us
+    rows = [{"Name": names["adamw"], "Calls": 12, "AverageNs": 2000, "MinNs": 1900, "MaxNs": 2100},
+            {"Name": names["pack"], "Calls": 12, "AverageNs": 1000, "MinNs": 900, "MaxNs": 1100},
+            {"Name": names["unpack"], "Calls": 12, "AverageNs": 1000, "MinNs": 900, "MaxNs": 1100},
+            {"Name": names["final"], "Calls": 12, "AverageNs": 3000, "MinNs": 2900, "MaxNs": 3100}]
+    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_stats.csv"),
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"], rows)
+    md = bench.stats_summary(str(tmp_path / "prof"), wl, steps=10, warmup=2)
+    assert "--steps 10 --warmup 2 --no-cpu-baseline --no-copy-ceiling" in md
+    assert "12 steps traced" in md
+    table = {line.split("|")[1].strip(): [c.strip() for c in line.split("|")[2:-1]]
+             for line in md.splitlines() if line.startswith("| ") and not line.startswith("| kernel |")}
+    adamw = table["adamw_vec_kernel<unsigned short>"]
+    assert adamw[0] == "12" and adamw[1] == "1.00" and adamw[2] == "2.0"
+    assert int(adamw[5]) == 28 * S
+    assert float(adamw[6]) == pytest.approx(28 * S / 2e-6 / 1e9, abs=0.1)
+    assert float(adamw[7]) == pytest.approx(100 * 28 * S / 2e-6 / 1e9 / 8000, abs=0.1)
+    assert int(table["copy_pieces_kernel<false>"][5]) == 4 * S
+    assert table["sqnorm_final_kernel"][5] == "-"
+
+
+@needs_lib
+def test_pmc_summary_calibration(tmp_path):
+    """FETCH_SIZE reading half the bytes and WRITE_SIZE all of them (as
+    measured on MI355X): the copy kernel calibrates factors 2 and 1, and a
+    kernel whose raw counters match its algorithmic bytes comes out at 1.0."""
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    copy, adamw = "copy_pieces_kernel<false>", "adamw_vec_kernel<unsigned short>"
+    raw = {copy: (2 * S / 1024 / 2, 2 * S / 1024), adamw: (14 * S / 1024 / 2, 14 * S / 1024 * 1.01)}
+    for counter, k in (("FETCH_SIZE", 0), ("WRITE_SIZE", 1)):
+        rows = [{"Kernel_Name": f"void (anonymous namespace)::{name}(x)", "Counter_Name": counter,
+                 "Counter_Value": vals[k]} for name, vals in raw.items() for _ in range(5)]
+        _write_csv(str(tmp_path / counter / "y" / "bench_counter_collection.csv"),
+                   ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    out = bench.pmc_summary(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), wl, steps=3, warmup=2)
+    assert out["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert out["calibration"]["write_factor"] == pytest.approx(1.0)
+    assert out["kernels"][copy]["traffic_over_algorithmic"] == pytest.approx(1.0)
+    a = out["kernels"][adamw]
+    assert a["algorithmic_bytes"] == 28 * S
+    assert a["traffic_bytes"] == pytest.approx(14 * S + 14 * S * 1.01, rel=1e-6)
+    assert a["traffic_over_algorithmic"] == pytest.approx(1.005, abs=1e-4)
+    assert "--steps 3 --warmup 2" in out["commands"][0]
+    json.dumps(out)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
