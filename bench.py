@@ -422,7 +422,7 @@ def offload_main(args, wl):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name} rank {rs.rank} of N_d={wl.n_d}, optimizer state offloaded to "
-                               f"host memory", "shard_params": S, "buckets": len(rs.pieces()),
+                               f"host memory", "shard_params": S, "buckets": len(rs.transfer_pieces()),
                    "staging_slots": len(rs.stage_g), "host_threads": rs.threads or len(os.sched_getaffinity(0))},
         "host_adamw_ms_per_step": host_s * 1e3,
         "host_adamw_params_per_s": S / host_s,

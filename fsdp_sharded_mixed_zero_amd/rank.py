@@ -257,8 +257,15 @@ class OffloadRank(RankShard):
     staging slot, the host updates it (zero_cpu_adamw_step), and the bf16
     parameters come back host->device before the GPU unpacks them. A ring of
     ``slots`` staging buffers and two copy streams let the PCIe copies of one
-    bucket overlap the host update of another. Shards without buckets are
-    split into pieces of ``bucket`` elements for this overlap."""
+    bucket overlap the host update of another.
+
+    Shards without buckets are staged in pieces of ``bucket`` elements, ramping
+    up from 1/8 of that size at the start and down again at the end: the
+    first download and the last upload are the parts nothing overlaps. Pack
+    and the norm keep the uniform ``pieces()``, so the norm's accumulation
+    order (and every result) is that of the all-GPU step. The views, events
+    and slots of every staged piece are made once, so the host thread, which
+    also runs a share of the update, spends little time between updates."""
 
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda", fill: bool = True,
                  bucket: int = 1 << 24, slots: int = 3, threads: int | None = None):
@@ -272,13 +279,36 @@ class OffloadRank(RankShard):
             self.move_state_to_host()
         self.threads = threads if threads is not None else int(
             os.environ.get("ZERO_CPU_THREADS", os.environ.get("OMP_NUM_THREADS", "0")) or 0)
-        piece = max(n for _, n in self.pieces())
+        staged = self.transfer_pieces()
+        piece = max(n for _, n in staged)
         self.stage_g = [torch.empty(piece, dtype=torch.int16, pin_memory=True) for _ in range(slots)]
         self.stage_p = [torch.empty(piece, dtype=torch.int16, pin_memory=True) for _ in range(slots)]
         self.h_rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, pin_memory=True)
         self.d2h = torch.cuda.Stream(device=self.device)
         self.h2d = torch.cuda.Stream(device=self.device)
         self.host_seconds = 0.0
+        g16, p16 = self.grad_shard.view(torch.int16), self.param_shard.view(torch.int16)
+        # per staged piece: begin, count, device gradient and parameter views,
+        # staging views, and the events marking its download and upload
+        self.plan = [(b, n, g16[b:b + n], p16[b:b + n], self.stage_g[i % slots][:n], self.stage_p[i % slots][:n],
+                      torch.cuda.Event(), torch.cuda.Event()) for i, (b, n) in enumerate(staged)]
+        self.packed = torch.cuda.Event()
+        self.sums_ready = torch.cuda.Event()
+
+    def transfer_pieces(self):
+        """The (begin, count) pieces staged through host memory."""
+        pieces = self.pieces()
+        if self.wl.bucket or len(pieces) < 4:
+            return pieces
+        B = self.bucket
+        ramp = [B >> 3, B >> 2, B >> 1]
+        mid = self.shard - 2 * sum(ramp)
+        sizes = ramp + [B] * (mid // B) + ([mid % B] if mid % B else []) + ramp[::-1]
+        out, b = [], 0
+        for n in sizes:
+            out.append((b, n))
+            b += n
+        return out
 
     def move_state_to_host(self, piece=1 << 26):
         """Copy the device state (drawn by fill_state) into host memory and
@@ -296,51 +326,40 @@ class OffloadRank(RankShard):
         hp = self.hparams(step)
         cs = torch.cuda.current_stream()
         stream = cs.cuda_stream
-        pieces = self.pieces()
         own = self.rank_sq[self.rank:self.rank + 1]
-        for k, (b, n) in enumerate(pieces):
+        for k, (b, n) in enumerate(self.pieces()):
             zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, b, n, own, k > 0,
                                         self.workspace, stream=stream)
-        packed = torch.cuda.Event()
-        packed.record(cs)
-        self.d2h.wait_event(packed)
+        self.packed.record(cs)
+        self.d2h.wait_event(self.packed)
+        plan, R = self.plan, len(self.stage_g)
         with torch.cuda.stream(self.d2h):
             self.h_rank_sq.copy_(self.rank_sq, non_blocking=True)
-        sums_ready = torch.cuda.Event()
-        sums_ready.record(self.d2h)
-
-        R = len(self.stage_g)
-        got, sent = [None] * len(pieces), [None] * len(pieces)
-
-        def fetch(i):
-            b, n = pieces[i]
-            with torch.cuda.stream(self.d2h):
-                self.stage_g[i % R][:n].copy_(self.grad_shard[b:b + n].view(torch.int16), non_blocking=True)
-            got[i] = torch.cuda.Event()
-            got[i].record(self.d2h)
-
-        for i in range(min(R, len(pieces))):
-            fetch(i)
-        sums_ready.synchronize()
-        for i, (b, n) in enumerate(pieces):
-            slot = i % R
-            got[i].synchronize()
+            self.sums_ready.record(self.d2h)
+            for _, _, g_dev, _, g_stage, _, got, _ in plan[:R]:
+                g_stage.copy_(g_dev, non_blocking=True)
+                got.record(self.d2h)
+        self.sums_ready.synchronize()
+        for i, (b, n, _, p_dev, g_stage, p_stage, got, sent) in enumerate(plan):
+            got.synchronize()
             if i >= R:
-                sent[i - R].synchronize()      # the staging slot's previous copy has left
+                plan[i - R][7].synchronize()      # the staging slot's previous upload has left
             t0 = time.perf_counter()
-            zero.zero_cpu_adamw_step(self.stage_g[slot], self.h_state, self.stage_p[slot], self.shard, b, n,
-                                     hp, self.h_rank_sq, self.wl.n_d, self.threads)
+            zero.zero_cpu_adamw_step(g_stage, self.h_state, p_stage, self.shard, b, n, hp, self.h_rank_sq,
+                                     self.wl.n_d, self.threads)
             self.host_seconds += time.perf_counter() - t0
             with torch.cuda.stream(self.h2d):
-                self.param_shard[b:b + n].view(torch.int16).copy_(self.stage_p[slot][:n], non_blocking=True)
-            sent[i] = torch.cuda.Event()
-            sent[i].record(self.h2d)
-            cs.wait_event(sent[i])
+                p_dev.copy_(p_stage, non_blocking=True)
+                sent.record(self.h2d)
+            if i + R < len(plan):                 # the next download into the slot just read
+                nxt = plan[i + R]
+                with torch.cuda.stream(self.d2h):
+                    nxt[4].copy_(nxt[2], non_blocking=True)
+                    nxt[6].record(self.d2h)
+            cs.wait_event(sent)
             zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs, b, n, stream)
-            if i + R < len(pieces):
-                fetch(i + R)
-        for ev in sent[-R:]:
-            ev.synchronize()                   # staging slots free for the next step
+        for entry in plan[-R:]:
+            entry[7].synchronize()                # staging slots free for the next step
 
     def pcie_bytes_per_step(self):
         """Bytes the step moves over PCIe: the bf16 gradients down, the bf16
