@@ -502,10 +502,36 @@ struct AdamWArgs {
   float lr_wd, step_size, inv_sqrt_bc2, eps;
 };
 
+// The clip coefficient from the ranks' partial sums, formed by every wave
+// (all 64 lanes must be active). G is added in a fixed two-level order: lane l
+// adds ranks l, l+64, l+128, ... in that order, and the 64 lane sums are then
+// added in lane order. With at most 64 ranks each lane holds one rank (the
+// others add nothing), so G is the plain rank-order sum, done here by one
+// loop of uniform loads. With more, each wave's loads are coalesced rows of 64
+// ranks and its dependent chain of fp64 adds is n_ranks/64 + 64 long instead
+// of n_ranks (a chain of 1024 made the update 8x slower). The host update
+// forms G in the same order.
 __device__ __forceinline__ float clip_coefficient(const AdamWArgs& a) {
   if (!a.clip_on) return 1.0f;
   double G = 0.0;
-  for (int r = 0; r < a.n_ranks; ++r) G += a.rank_sq[r];
+  if (a.n_ranks <= 64) {
+    for (int r = 0; r < a.n_ranks; ++r) G += a.rank_sq[r];   // uniform loads, rank order
+  } else {
+    const int lane = threadIdx.x & 63;
+    const int rows = a.n_ranks >> 6;
+    double run = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < rows; ++j) run += a.rank_sq[(j << 6) + lane];
+    if (lane < a.n_ranks - (rows << 6)) run += a.rank_sq[(rows << 6) + lane];
+    const unsigned long long bits = __double_as_longlong(run);
+    const int lo = int(unsigned(bits)), hi = int(unsigned(bits >> 32));
+#pragma unroll
+    for (int l = 0; l < 64; ++l) {   // lane l's sum, read into scalar registers
+      const unsigned long long u = (unsigned long long)unsigned(__builtin_amdgcn_readlane(lo, l)) |
+                                   ((unsigned long long)unsigned(__builtin_amdgcn_readlane(hi, l)) << 32);
+      G += __longlong_as_double((long long)u);
+    }
+  }
   const double ratio = a.max_norm / (sqrt(G) + a.clip_eps);
   return float(ratio >= 1.0 ? 1.0 : ratio);  // a NaN ratio stays NaN
 }

@@ -211,8 +211,15 @@ int cpu_adamw(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t
   a.eps = float(hp->eps);
   a.coef = 1.0f;
   if (clip) {
+    // the GPU update's order: lane sums of ranks l, l+64, l+128, ... (each in
+    // rank order), then the 64 lane sums in order (for at most 64 ranks, the
+    // plain rank-order sum)
     double G2 = 0.0;
-    for (int32_t r = 0; r < n_ranks; ++r) G2 += h_rank_sqnorms[r];
+    for (int32_t l = 0; l < 64; ++l) {
+      double run = 0.0;
+      for (int64_t r = l; r < n_ranks; r += 64) run += h_rank_sqnorms[r];
+      G2 += run;
+    }
     const double ratio = hp->max_norm / (std::sqrt(G2) + hp->clip_eps);
     a.coef = float(ratio >= 1.0 ? 1.0 : ratio);   // a NaN ratio stays NaN
   }

@@ -216,7 +216,9 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
  * state per parameter (section 2 of the lesson; notes section 2.1).
  * Per element, with g the bf16 gradient widened to fp32:
  *   c  = clip coefficient from G = d_rank_sqnorms[0] + ... + d_rank_sqnorms[n_ranks-1]
- *        (added in that order in fp64)
+ *        in fp64, in a fixed order: for at most 64 ranks, rank order; beyond,
+ *        64 lane sums (lane l adds ranks l, l+64, l+128, ... in order), then
+ *        the lane sums in lane order
  *   g' = c*g;  m = beta1*m + (1-beta1)*g';  v = beta2*v + (1-beta2)*g'^2
  *   master = master*(1 - lr*wd) - (lr/(1-beta1^t)) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
  *   param  = bf16 round-to-nearest-even of the new fp32 master
@@ -309,7 +311,8 @@ int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* c
  *             begin first): a staging buffer the caller fills from the GPU
  *   h_state   HOST pointer to the tiled fp32 state of all n_state elements
  *   h_param   HOST array receiving the count bf16 parameters of the range
- *   h_rank_sqnorms  HOST array of n_ranks doubles
+ *   h_rank_sqnorms  HOST array of n_ranks doubles, added in zero_adamw_step's
+ *             order
  *   n_threads host threads to use (0 = all the process may run on); the
  *             library keeps its threads for the life of the process, and
  *             concurrent calls run one after another

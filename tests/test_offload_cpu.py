@@ -60,6 +60,11 @@ def test_cpu_adamw_sub_ranges(begin, count):
     _case(3 * TILE + 10, begin, count, 2, O.AdamWHParams(), 2, 3, seed=begin + 17 * count)
 
 
+@pytest.mark.parametrize("n_ranks", [1, 63, 64, 65, 1000, 4097])
+def test_cpu_adamw_many_ranks(n_ranks):
+    _case(20_000, 0, 20_000, 2, O.AdamWHParams(), n_ranks, 2, seed=n_ranks)
+
+
 @pytest.mark.parametrize("step", [1, 1000])
 def test_cpu_adamw_hyperparameters(step):
     for ohp in (O.AdamWHParams(max_norm=0.0),
