@@ -78,12 +78,26 @@ def oracle_partial(grad_shard, S):
     return total
 
 
-@pytest.mark.parametrize("fused_norm", [True, False], ids=["fused-norm", "separate-norm"])
-@pytest.mark.parametrize("name", ["gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b"])
-def test_workload_full_size(name, fused_norm):
+# (workload, fused norm, bucket): None keeps the workload's own bucketing. The
+# 70B shard in one piece makes a single AdamW launch of 2.2e9 four-element
+# units, more than its 2^23-block grid holds, so that launch strides; the
+# fused pack then covers 8.6e9 elements in two launches and its final sum
+# adds ~1e6 block partials.
+FULL_SIZE = ([(n, f, None) for n in ("gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b") for f in (True, False)]
+             + [("llama-70b", True, 0)])
+
+
+@pytest.mark.parametrize("name,fused_norm,bucket", FULL_SIZE,
+                         ids=[f"{n}-{'fused' if f else 'separate'}-norm{'-one-piece' if b == 0 else ''}"
+                              for n, f, b in FULL_SIZE])
+def test_workload_full_size(name, fused_norm, bucket):
+    import dataclasses
+
     from fsdp_sharded_mixed_zero_amd.rank import RankShard
 
     wl = synth.WORKLOADS[name]
+    if bucket is not None:
+        wl = dataclasses.replace(wl, bucket=bucket)
     lay = build_layout(wl.sizes, wl.n_d, wl.rank, wl.align)
     S = lay.shard
     rng = np.random.default_rng(len(wl.sizes))
