@@ -121,10 +121,15 @@ def _check(func, rc):
 
 
 def _ptr(x):
+    """Device address of a torch tensor (or an integer address). A host
+    tensor or array is refused here: a kernel would read a host address."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise TypeError(f"device memory expected, got {type(x).__name__}"
+                        f"{' on ' + str(x.device) if hasattr(x, 'device') else ''}")
     return x.data_ptr()
 
 
@@ -263,11 +268,14 @@ def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count:
 
 
 def _host_ptr(x):
-    """Address of a host buffer: a CPU torch tensor, a numpy array or an int."""
+    """Address of a host buffer: a CPU torch tensor, a numpy array or an int.
+    A device tensor is refused: the host update would read a device address."""
     if x is None or isinstance(x, int):
         return x
     if hasattr(x, "ctypes"):
         return x.ctypes.data
+    if getattr(x, "is_cuda", False):
+        raise TypeError("host memory expected, got a device tensor")
     return x.data_ptr()
 
 

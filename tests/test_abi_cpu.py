@@ -178,3 +178,19 @@ def test_segments_query_with_small_capacity():
     assert lib.zero_layout_segments(lay.handle, segs, 1, ctypes.byref(n)) == 0
     assert n.value == 3 and segs[0].len == 10
     assert lib.zero_layout_segments(lay.handle, None, 2, ctypes.byref(n)) == zero.ZERO_EINVAL
+
+
+def test_binding_refuses_memory_on_the_wrong_side():
+    """Host buffers given to a device entry point (and device buffers given to
+    the host update) are refused by the binding before anything runs."""
+    torch = pytest.importorskip("torch")
+    import numpy as np
+
+    x = torch.zeros(8, dtype=torch.float32)
+    hp = zero.hparams(step=1)
+    with pytest.raises(TypeError):
+        zero.zero_adamw_step(x, x, x, 8, 0, 8, hp, None, 0)
+    with pytest.raises(TypeError):
+        zero.zero_accumulate_grads(np.zeros(8, np.uint16), x, 8, True)
+    with pytest.raises(TypeError):
+        zero.zero_state_import(x, x, x, x, 8)
