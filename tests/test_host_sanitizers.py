@@ -1,0 +1,46 @@
+"""The library's host code (the partitioner and the host AdamW with its thread
+pool) under AddressSanitizer and UndefinedBehaviorSanitizer: a host-only
+build of layout.cpp and offload.cpp (device entry points stubbed) runs the
+host tests in a child process with the sanitizer runtime preloaded. Any
+report aborts the child. Skipped where ROCm's clang or its sanitizer runtime
+is missing."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "fsdp_sharded_mixed_zero_amd", "csrc")
+CLANG = "/opt/rocm/lib/llvm/bin/clang++"
+
+# host tests that do not reach the (stubbed) device entry points
+HOST_TESTS = ["tests/test_offload_cpu.py", "tests/test_oracle_layout.py", "tests/test_abi_cpu.py"]
+DESELECT = "not device_calls_reject and not workspace_size_is_bounded"
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    if not os.path.exists(CLANG):
+        pytest.skip("ROCm clang++ not found")
+    runtime = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                             text=True).stdout.strip()
+    if not os.path.isabs(runtime) or not os.path.exists(runtime):
+        pytest.skip("sanitizer runtime not found")
+    lib = str(tmp_path / "libzero_host_sanitized.so")
+    build = [CLANG, "-shared", "-fPIC", "-O1", "-g", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan",
+             "-std=c++17", "-fno-math-errno", "-ffp-contract=off", "-D__HIP_PLATFORM_AMD__",
+             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", "/opt/rocm/include",
+             os.path.join(CSRC, "layout.cpp"), os.path.join(CSRC, "offload.cpp"),
+             os.path.join(ROOT, "tests", "sanitize", "device_stubs.cpp"), "-pthread", "-o", lib]
+    r = subprocess.run(build, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, LD_PRELOAD=runtime, ZERO_MI355X_LIB=lib,
+               ASAN_OPTIONS="detect_leaks=0:alloc_dealloc_mismatch=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+                        "-k", DESELECT, *HOST_TESTS], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=900)
+    assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
+    assert " passed" in r.stdout
