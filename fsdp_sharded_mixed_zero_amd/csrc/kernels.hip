@@ -572,8 +572,9 @@ __device__ __forceinline__ f32x4 grad4(const AdamWArgs& a, int64_t e) {
   }
 }
 
+// One element; returns the bf16 parameter it stores.
 template <typename G>
-__device__ __forceinline__ void adamw_scalar(const AdamWArgs& a, float c, int64_t e) {
+__device__ __forceinline__ uint16_t adamw_scalar(const AdamWArgs& a, float c, int64_t e) {
   int64_t L;
   float* s = tile_slot(a, e, &L);
   float p = s[0], m = s[L], v = s[2 * L];
@@ -581,7 +582,9 @@ __device__ __forceinline__ void adamw_scalar(const AdamWArgs& a, float c, int64_
   s[0] = p;
   s[L] = m;
   s[2 * L] = v;
-  a.param[e] = to_bf16(p);
+  const uint16_t b = to_bf16(p);
+  a.param[e] = b;
+  return b;
 }
 
 template <typename G>
@@ -631,6 +634,136 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_elem_kernel(const AdamWArg
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
   for (int64_t e = a.begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; e < a.end; e += stride)
     adamw_scalar<G>(a, c, e);
+}
+
+// ------------------------------------------------ AdamW with the unpack fused
+//
+// The same update, and each new bf16 parameter is also stored at its
+// position in the per-tensor parameters: AdamW followed by unpack over the
+// same range, in one pass (30 instead of 28 + 4 bytes per element). The
+// parameter shard is still written (it is what the all-gather sends). One
+// launch carries up to kUnpackMaxPieces pieces of the range in its kernel
+// arguments; inside a rank's shard they are contiguous, and padding (after
+// the last) has no tensor. Each wave finds the piece of its lowest element
+// (uniform loads); when the whole wave lies in it, a lane stores its 4 values
+// with one 8-byte store (or 4 scalar stores when the tensor is not 8-byte
+// congruent with the shard); a wave across a piece boundary loops over the
+// pieces it touches. Every table index is wave-uniform.
+
+constexpr int kUnpackMaxPieces = 64;
+constexpr int kWave = 64;
+
+struct UnpackPieces {
+  int32_t n;                               // pieces (0: no tensor element in the range)
+  int32_t _pad;
+  uint64_t vec_mask;                       // bit p: 4-element stores to piece p are 8-byte aligned
+  int64_t lo[kUnpackMaxPieces + 1];        // piece p holds shard elements [lo[p], lo[p+1]); lo[n] ends the last
+  uint16_t* dst[kUnpackMaxPieces];         // tensor element of shard element lo[p]
+};
+static_assert(sizeof(AdamWArgs) + sizeof(UnpackPieces) <= 4096, "kernel arguments fit the 4 KiB segment");
+
+// The value x holds in the wave's first active lane.
+__device__ __forceinline__ int64_t wave_first(int64_t x) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(x)))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(uint64_t(x) >> 32))));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// The piece holding shard element e (uniform; lo[0] <= e): the last p with lo[p] <= e.
+__device__ __forceinline__ int unpack_piece(const UnpackPieces& U, int64_t e) {
+  int lo = 0, hi = U.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (U.lo[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Store the bf16 values of this lane's shard elements [e, e + N) (N = 1 or 4;
+// for 4, packed in two words) at their tensor positions. The active lanes of
+// the wave hold consecutive elements starting at the first active lane's, all
+// within W elements of it.
+template <int N, int W>
+__device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, uint32_t w0, uint32_t w1) {
+  if (U.n == 0) return;
+  const int64_t w_lo = wave_first(e);
+  if (w_lo >= U.lo[U.n]) return;                     // padding only
+  int p = w_lo < U.lo[0] ? 0 : unpack_piece(U, w_lo);
+  if (w_lo >= U.lo[p] && w_lo + W <= U.lo[p + 1]) {  // the whole wave lies in piece p
+    uint16_t* d = U.dst[p] + (e - U.lo[p]);
+    if constexpr (N == 4) {
+      if ((U.vec_mask >> p) & 1) {
+        __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(d));
+      } else {
+        d[0] = uint16_t(w0);
+        d[1] = uint16_t(w0 >> 16);
+        d[2] = uint16_t(w1);
+        d[3] = uint16_t(w1 >> 16);
+      }
+    } else {
+      d[0] = uint16_t(w0);
+    }
+    return;
+  }
+  for (; p < U.n && U.lo[p] < w_lo + W; ++p) {       // the pieces the wave touches
+    const int64_t lo = U.lo[p], hi = U.lo[p + 1];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int64_t ek = e + k;
+      const uint32_t w = k < 2 ? w0 : w1;
+      if (ek >= lo && ek < hi) U.dst[p][ek - lo] = uint16_t(k & 1 ? w >> 16 : w);
+    }
+  }
+}
+
+template <typename G>
+__global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const AdamWArgs a, const UnpackPieces U) {
+  const float c = clip_coefficient(a);
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  for (int64_t u = a.u_begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < a.u_end; u += stride) {
+    const int64_t e = u << 2;
+    int64_t L;
+    float* s = tile_slot(a, e, &L);
+    if (L & 3) {   // a compact last tile whose m and v are not 16-byte aligned
+      for (int k = 0; k < 4; ++k) unpack_lane<1, 4 * kWave>(U, e + k, adamw_scalar<G>(a, c, e + k), 0);
+      continue;
+    }
+    f32x4* ps = reinterpret_cast<f32x4*>(s);
+    f32x4* ms = reinterpret_cast<f32x4*>(s + L);
+    f32x4* vs = reinterpret_cast<f32x4*>(s + 2 * L);
+    const f32x4 g4 = grad4<G>(a, e);
+    const f32x4 p4 = __builtin_nontemporal_load(ps);
+    const f32x4 m4 = __builtin_nontemporal_load(ms);
+    const f32x4 v4 = __builtin_nontemporal_load(vs);
+    float p[4] = {p4[0], p4[1], p4[2], p4[3]};
+    float m[4] = {m4[0], m4[1], m4[2], m4[3]};
+    float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) adamw_one(a, c, g4[k], p[k], m[k], v[k]);
+    __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, ps);
+    __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, ms);
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, vs);
+    const uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
+    __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(a.param + e));
+    unpack_lane<4, 4 * kWave>(U, e, w0, w1);
+  }
+  // up to 3 elements before the first unit and after the last one
+  if (blockIdx.x == 0) {
+    const int t = threadIdx.x;
+    const int64_t head_end = 4 * a.u_begin < a.end ? 4 * a.u_begin : a.end;
+    if (t < 4 && a.begin + t < head_end)
+      unpack_lane<1, 4>(U, a.begin + t, adamw_scalar<G>(a, c, a.begin + t), 0);
+    const int64_t k = 4 * a.u_end + (t - 4);
+    if (t >= 4 && t < 8 && k >= head_end && k < a.end) unpack_lane<1, 4>(U, k, adamw_scalar<G>(a, c, k), 0);
+  }
+}
+
+template <typename G>
+__global__ __launch_bounds__(kAdamThreads) void adamw_unpack_elem_kernel(const AdamWArgs a, const UnpackPieces U) {
+  const float c = clip_coefficient(a);
+  const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
+  for (int64_t e = a.begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; e < a.end; e += stride)
+    unpack_lane<1, kWave>(U, e, adamw_scalar<G>(a, c, e), 0);
 }
 
 // ------------------------------------------------ fp32 gradient accumulation
@@ -813,10 +946,13 @@ extern "C" int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* 
   return zero::ok();
 }
 
+// Checks the arguments of an update over [begin, begin+count) and fills the
+// kernel arguments (range fields for the whole range). *vec: the pointers
+// allow the vector path.
 template <typename G>
-static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
-                        int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
-                        int32_t n_ranks, hipStream_t stream, const char* who) {
+static int adamw_args(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
+                      int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms, int32_t n_ranks,
+                      const char* who, AdamWArgs* out, bool* vec) {
   if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
   if (n_state < 0 || begin < 0 || count < 0 || begin > n_state || count > n_state - begin)
     return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside a state of %lld elements", who, (long long)begin,
@@ -835,11 +971,6 @@ static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int6
   a.state = d_state;
   a.param = d_param;
   a.n_state = n_state;
-  a.begin = begin;
-  a.end = begin + count;
-  a.u_begin = (begin + 3) >> 2;
-  a.u_end = a.end >> 2;
-  if (a.u_end < a.u_begin) a.u_end = a.u_begin;   // fewer than 4 elements, all scalar
   a.rank_sq = d_rank_sqnorms;
   a.n_ranks = clip ? n_ranks : 0;
   a.clip_on = clip ? 1 : 0;
@@ -856,18 +987,90 @@ static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int6
   a.step_size = float(hp->lr / bc1);
   a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
   a.eps = float(hp->eps);
-
   // vector path: 4 gradients (8 or 16 bytes), 4 bf16 params (8 bytes), fp32 state (16 bytes)
-  const bool vec = aligned(d_grad, 4 * sizeof(G)) && aligned(d_param, 8) && aligned(d_state, 16);
-  const int64_t work = vec ? std::max<int64_t>(a.u_end - a.u_begin, 1) : count;
+  *vec = aligned(d_grad, 4 * sizeof(G)) && aligned(d_param, 8) && aligned(d_state, 16);
+  *out = a;
+  return zero::ok();
+}
+
+// Sets a's range to [r0, r1) and returns the grid for it.
+static unsigned adamw_range(AdamWArgs* a, int64_t r0, int64_t r1, bool vec) {
+  a->begin = r0;
+  a->end = r1;
+  a->u_begin = (r0 + 3) >> 2;
+  a->u_end = r1 >> 2;
+  if (a->u_end < a->u_begin) a->u_end = a->u_begin;   // fewer than 4 elements, all scalar
+  const int64_t work = vec ? std::max<int64_t>(a->u_end - a->u_begin, 1) : r1 - r0;
   int64_t blocks = (work + kAdamThreads - 1) / kAdamThreads;
-  blocks = std::min(std::max<int64_t>(blocks, 1), kAdamMaxBlocks);
+  return unsigned(std::min(std::max<int64_t>(blocks, 1), kAdamMaxBlocks));
+}
+
+template <typename G>
+static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
+                        int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
+                        int32_t n_ranks, hipStream_t stream, const char* who) {
+  AdamWArgs a{};
+  bool vec = false;
+  if (int rc = adamw_args(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks, who, &a,
+                          &vec))
+    return rc;
+  if (count == 0) return zero::ok();
+  const unsigned blocks = adamw_range(&a, begin, begin + count, vec);
   if (vec)
-    hipLaunchKernelGGL(adamw_vec_kernel<G>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+    hipLaunchKernelGGL(adamw_vec_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(adamw_elem_kernel<G>, dim3(unsigned(blocks)), dim3(kAdamThreads), 0, stream, a);
+    hipLaunchKernelGGL(adamw_elem_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+// The update with the unpack fused: one launch per run of up to
+// kUnpackMaxPieces pieces of the range; the last launch also covers the
+// padding after the last piece.
+template <typename G>
+static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
+                               int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
+                               int32_t n_ranks, zero_layout_t h, uint16_t* const* tensor_params, hipStream_t stream,
+                               const char* who) {
+  if (h == nullptr || tensor_params == nullptr) return fail(ZERO_EINVAL, "%s: NULL handle or tensor array", who);
+  if (n_state != h->info.shard)
+    return fail(ZERO_EINVAL, "%s: n_state %lld is not the layout's shard of %lld elements", who,
+                (long long)n_state, (long long)h->info.shard);
+  AdamWArgs a{};
+  bool vec = false;
+  if (int rc = adamw_args(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks, who, &a,
+                          &vec))
+    return rc;
+  if (count == 0) return zero::ok();
+  std::vector<Piece> pieces;
+  if (int rc = build_pieces(h, tensor_params, d_param, begin, count, false, &pieces, who)) return rc;
+  const int64_t end = begin + count;
+  size_t i = 0;
+  int64_t r0 = begin;
+  do {
+    UnpackPieces U{};
+    int n = 0;
+    for (; i < pieces.size() && n < kUnpackMaxPieces; ++i, ++n) {
+      const int64_t lo = pieces[i].src - d_param;            // the piece's first shard element
+      if (lo != (n == 0 ? r0 : U.lo[n]))
+        return fail(ZERO_EINVAL, "%s: internal error: pieces not contiguous at element %lld", who, (long long)lo);
+      U.lo[n] = lo;
+      U.lo[n + 1] = lo + pieces[i].len;
+      U.dst[n] = pieces[i].dst;
+      if (((uintptr_t(pieces[i].dst) - 2 * uintptr_t(lo)) & 7u) == 0) U.vec_mask |= uint64_t(1) << n;
+    }
+    U.n = n;
+    const int64_t r1 = i < pieces.size() ? U.lo[n] : end;
+    const unsigned blocks = adamw_range(&a, r0, r1, vec);
+    if (vec)
+      hipLaunchKernelGGL(adamw_unpack_vec_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a, U);
+    else
+      hipLaunchKernelGGL(adamw_unpack_elem_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a, U);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    r0 = r1;
+  } while (i < pieces.size());
   return zero::ok();
 }
 
@@ -907,6 +1110,23 @@ extern "C" int zero_adamw_step_f32grad(const float* d_grad, float* d_state, uint
                                        const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream) {
   return adamw_launch<float>(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks,
                              stream, "zero_adamw_step_f32grad");
+}
+
+extern "C" int zero_adamw_step_unpack(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
+                                      int64_t begin, int64_t count, const zero_adamw_hparams* hp,
+                                      const double* d_rank_sqnorms, int32_t n_ranks, zero_layout_t h,
+                                      uint16_t* const* tensor_params, hipStream_t stream) {
+  return adamw_unpack_launch<uint16_t>(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms,
+                                       n_ranks, h, tensor_params, stream, "zero_adamw_step_unpack");
+}
+
+extern "C" int zero_adamw_step_f32grad_unpack(const float* d_grad, float* d_state, uint16_t* d_param,
+                                              int64_t n_state, int64_t begin, int64_t count,
+                                              const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
+                                              int32_t n_ranks, zero_layout_t h, uint16_t* const* tensor_params,
+                                              hipStream_t stream) {
+  return adamw_unpack_launch<float>(d_grad, d_state, d_param, n_state, begin, count, hp, d_rank_sqnorms, n_ranks,
+                                    h, tensor_params, stream, "zero_adamw_step_f32grad_unpack");
 }
 
 extern "C" int zero_accumulate_grads(const uint16_t* d_grad, float* d_acc, int64_t count, int32_t first,

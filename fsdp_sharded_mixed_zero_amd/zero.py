@@ -80,6 +80,12 @@ _SIGNATURES = {
                                        ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
     "zero_adamw_step_f32grad": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                                ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
+    "zero_adamw_step_unpack": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
+                                              ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP,
+                                              ctypes.POINTER(_VP), _VP]),
+    "zero_adamw_step_f32grad_unpack": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
+                                                      ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP,
+                                                      ctypes.POINTER(_VP), _VP]),
     "zero_accumulate_grads": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
     "zero_cpu_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                            ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _I32]),
@@ -265,6 +271,23 @@ def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count:
     _check("zero_adamw_step_f32grad", library().zero_adamw_step_f32grad(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def zero_adamw_step_unpack(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
+                           rank_sqnorms, n_ranks: int, layout: Layout, tensor_params, stream=None):
+    arr = _ptr_array(tensor_params)
+    _check("zero_adamw_step_unpack", library().zero_adamw_step_unpack(
+        _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))
+
+
+def zero_adamw_step_f32grad_unpack(grad, state, param, n_state: int, begin: int, count: int,
+                                   hp: zero_adamw_hparams, rank_sqnorms, n_ranks: int, layout: Layout,
+                                   tensor_params, stream=None):
+    arr = _ptr_array(tensor_params)
+    _check("zero_adamw_step_f32grad_unpack", library().zero_adamw_step_f32grad_unpack(
+        _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))
 
 
 def _host_ptr(x):

@@ -15,5 +15,7 @@ int zero_state_export(const float*, float*, float*, float*, int64_t, hipStream_t
 int zero_accumulate_grads(const uint16_t*, float*, int64_t, int32_t, hipStream_t) { return -1; }
 int zero_shard_sqnorm_f32(const float*, int64_t, double*, int32_t, void*, size_t, hipStream_t) { return -1; }
 int zero_adamw_step_f32grad(const float*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, hipStream_t) { return -1; }
+int zero_adamw_step_unpack(const uint16_t*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, zero_layout_t, uint16_t* const*, hipStream_t) { return -1; }
+int zero_adamw_step_f32grad_unpack(const float*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, zero_layout_t, uint16_t* const*, hipStream_t) { return -1; }
 int zero_unpack_params(zero_layout_t, const uint16_t*, uint16_t* const*, int64_t, int64_t, hipStream_t) { return -1; }
 }

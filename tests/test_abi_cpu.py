@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     lib = zero.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -141,6 +141,18 @@ def test_device_calls_reject_bad_arguments_on_the_host():
     assert lib.zero_adamw_step_f32grad(None, None, None, 8, 0, 8, ctypes.byref(hp), None, 1,
                                        None) == zero.ZERO_EINVAL
     assert lib.zero_state_export(None, None, None, None, 5, None) == zero.ZERO_EINVAL
+    # the update with the unpack fused: layout handle and shard size checked first
+    lay = zero.zero_layout([100, 28], 1, 0, 1)
+    arr = (ctypes.c_void_p * 2)()
+    for fn in (lib.zero_adamw_step_unpack, lib.zero_adamw_step_f32grad_unpack):
+        assert fn(None, None, None, 128, 0, 8, ctypes.byref(hp), None, 1, None, arr, None) == zero.ZERO_EINVAL
+        assert fn(None, None, None, 100, 0, 8, ctypes.byref(hp), None, 1, lay.handle, arr,
+                  None) == zero.ZERO_EINVAL
+        assert "shard" in zero.zero_last_error()
+        assert fn(None, None, None, 128, 0, 8, ctypes.byref(hp), None, 1, lay.handle, arr,
+                  None) == zero.ZERO_EINVAL                      # NULL buffers with work to do
+        off = zero.hparams(max_norm=0.0, step=1)
+        assert fn(None, None, None, 128, 3, 0, ctypes.byref(off), None, 0, lay.handle, arr, None) == zero.ZERO_OK
 
 
 def test_state_tile_constant_matches_header():
