@@ -46,6 +46,8 @@ def parse():
                     help="run pack and the sum of squares as two calls instead of the fused one")
     ap.add_argument("--accum", type=int, default=1, metavar="K",
                     help="fp32 gradient accumulation over K micro-batches per step (K > 1)")
+    ap.add_argument("--separate-unpack", action="store_true",
+                    help="run AdamW and the unpack as two calls instead of the fused one")
     ap.add_argument("--flat", action="store_true",
                     help="ZeRO-1 flat buffers: gradients and parameters are views into flat buffers, the "
                          "shard is the rank's slice (no pack, no unpack)")
@@ -74,10 +76,24 @@ def kernel_name(raw):
     return name.split("(")[0].split("::")[-1]
 
 
-def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False):
+def update_kernel(accum=1, separate_unpack=False, flat=False):
+    """The update kernel of a mode (the roofline's dominant kernel)."""
+    grad = "float" if accum > 1 else "unsigned short"
+    fused = not separate_unpack and not flat
+    return f"adamw_unpack_vec_kernel<{grad}>" if fused else f"adamw_vec_kernel<{grad}>"
+
+
+def ceiling_elems(launch_bytes):
+    """bf16 elements of the copy ceiling's buffers for an update launch of
+    ``launch_bytes`` (the copy moves 4 bytes per element)."""
+    return max(8, min(int(launch_bytes), 8 << 30) // 4 // 8 * 8)
+
+
+def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unpack=False):
     """Algorithmic HBM bytes per step of each kernel over the whole shard, for
-    the benchmark's mode (fused norm by default, separate norm, fp32
-    accumulation over ``accum`` micro-batches, or flat buffers)."""
+    the benchmark's mode (fused norm and fused unpack by default, separate
+    norm, separate unpack, fp32 accumulation over ``accum`` micro-batches, or
+    flat buffers)."""
     from fsdp_sharded_mixed_zero_amd import zero
     info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
     S = info["shard"]
@@ -85,26 +101,32 @@ def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False):
     pack = 4 * real + 2 * (S - real)
     if flat:
         return S, real, {"sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel<unsigned short>": 28 * S}
-    out = {"copy_pieces_kernel<false>": 4 * real}          # unpack
+    update = update_kernel(accum, separate_unpack)
+    out = {}
+    if separate_unpack:
+        out["copy_pieces_kernel<false>"] = 4 * real          # unpack
     if accum > 1:
-        out["copy_pieces_kernel<false>"] += accum * pack   # plus one pack per micro-batch
+        out["copy_pieces_kernel<false>"] = out.get("copy_pieces_kernel<false>", 0) + accum * pack   # packs
         out.update({"accumulate_kernel": (6 + 10 * (accum - 1)) * S, "sqnorm_f32_partial_kernel": 4 * S,
-                    "adamw_vec_kernel<float>": 30 * S})
+                    update: 30 * S})
     else:
         if separate_norm:
-            out["copy_pieces_kernel<false>"] += pack
+            out["copy_pieces_kernel<false>"] = out.get("copy_pieces_kernel<false>", 0) + pack
             out["sqnorm_partial_kernel"] = 2 * S
         else:
             out["copy_pieces_kernel<true>"] = pack
-        out["adamw_vec_kernel<unsigned short>"] = 28 * S
+        out[update] = 28 * S
+    if not separate_unpack:
+        out[update] += 2 * real                                # the tensor writes of the fused unpack
     return S, real, out
 
 
 def steps_traced(counts, wl, S):
-    """Steps a trace covers (warm-up included), from the AdamW launches."""
+    """Steps a trace covers (warm-up included): the sum-of-squares final
+    kernel runs once per bucket in every mode, whereas an update over more
+    than 64 tensor pieces takes several launches."""
     pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
-    adamw = next(k for k in counts if k.startswith("adamw_vec_kernel"))
-    return counts[adamw] / pieces
+    return counts["sqnorm_final_kernel"] / pieces
 
 
 def source_hash():
@@ -117,11 +139,13 @@ def traffic_file(workload):
     return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
-def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, accum=1, separate_norm=False):
+def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=False):
     """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
-    for the copy kernel of known size (the plain copy_pieces_kernel: unpack
-    reads and writes 2 bytes per real shard element)."""
+    for a plain copy of known size: by default the copy ceiling's copy (the
+    library's plain copy kernel over the ceiling's buffers, run in the same
+    benchmark), with --separate-unpack the unpack (2 bytes read and written
+    per real shard element)."""
     import csv
     import glob
 
@@ -136,20 +160,25 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, accum=1, separate_
 
     fetch, n_f = load(fetch_dir, "FETCH_SIZE")
     write, n_w = load(write_dir, "WRITE_SIZE")
-    mode = (f"--steps {steps} --warmup {warmup}" + (f" --accum {accum}" if accum > 1 else "") +
-            (" --separate-norm" if separate_norm else ""))
-    S, real, algo = algorithmic_bytes(wl, accum, separate_norm)
+    mode = f"--steps {steps} --warmup {warmup}" + (" --separate-unpack --no-copy-ceiling" if separate_unpack else "")
+    S, real, algo = algorithmic_bytes(wl, separate_unpack=separate_unpack)
     steps = steps_traced(n_f, wl, S)
-    # the plain copy (unpack) reads and writes exactly 2 bytes per real element
-    copy = "copy_pieces_kernel<false>"
+    update = update_kernel(separate_unpack=separate_unpack)
     per_dispatch = {k: algo[k] / (n_f[k] / steps) for k in algo if k in n_f}
-    known_read = per_dispatch[copy] / 2 / 1024.0       # KiB per dispatch
-    known_write = per_dispatch[copy] / 2 / 1024.0
-    f_fetch = known_read / fetch[copy]
-    f_write = known_write / write[copy]
+    copy = "copy_pieces_kernel<false>"
+    if separate_unpack:
+        known = per_dispatch[copy] / 2               # unpack: as many bytes read as written
+        source = "the unpack (2 bytes read and written per real shard element)"
+    else:
+        known = 2 * ceiling_elems(per_dispatch[update])  # the copy ceiling's copy: 2 bytes each way per element
+        per_dispatch[copy] = 2 * known
+        source = "the copy ceiling's plain copy of the same benchmark run"
+    known_kib = known / 1024.0
+    f_fetch = known_kib / fetch[copy]
+    f_write = known_kib / write[copy]
     kernels = {}
     for k in fetch:
-        if k not in algo and not k.startswith("sqnorm_final"):
+        if k not in per_dispatch and not k.startswith("sqnorm_final"):
             continue
         bytes_ = (fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024.0
         kernels[k] = {"fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
@@ -159,19 +188,19 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, accum=1, separate_
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline --no-copy-ceiling",
+                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline --no-copy-ceiling",
+                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline",
                 f"python bench.py --workload {wl.name} {mode} --pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
             "kernel_source_sha256": source_hash(),
-            "calibration": {"kernel": copy, "known_read_kib": known_read,
-                            "known_write_kib": known_write, "fetch_factor": round(f_fetch, 5),
+            "calibration": {"kernel": copy, "source": source, "known_read_kib": known_kib,
+                            "known_write_kib": known_kib, "fetch_factor": round(f_fetch, 5),
                             "write_factor": round(f_write, 5)},
             "kernels": kernels}
 
 
-def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False):
+def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False, separate_unpack=False):
     """Markdown table of a rocprofv3 kernel-stats CSV of this benchmark, with
     achieved bandwidth from each kernel's algorithmic bytes per launch (the
     step's bytes spread over that kernel's launches per step)."""
@@ -179,11 +208,11 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     import glob
 
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
-    S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat)
+    S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat, separate_unpack)
     rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
     steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S)
     mode = ((f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "") +
-            (" --flat" if flat else ""))
+            (" --flat" if flat else "") + (" --separate-unpack" if separate_unpack else ""))
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
              f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
              "Command (repository root, one MI355X):", "",
@@ -350,16 +379,15 @@ def cpu_baseline_parallel(wl, seconds, workers):
                        f"({sum(d for d, _ in out)} elements in all)")}
 
 
-def copy_ceiling(torch, nbytes, reps=20):
-    """The streaming ceiling the kernels are compared with: a plain copy that
-    moves ``nbytes`` per launch (half read, half written), timed with HIP
-    events around each launch like the kernels. The copy is the library's
+def copy_ceiling(torch, n, reps=20):
+    """The streaming ceiling the kernels are compared with: a plain copy of
+    ``n`` bf16 elements per launch (4n bytes, half read, half written), timed
+    with HIP events around each launch like the kernels. The copy is the library's
     unpack over a one-tensor layout (one piece: the plain copy kernel);
     torch's device-to-device ``copy_`` of the same bytes is listed beside it."""
     from fsdp_sharded_mixed_zero_amd import zero
 
-    n = max(8, nbytes // 4 // 8 * 8)       # bf16 elements; the copy moves 4 bytes each
-    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")   # the copy moves 4 bytes per element
     dst = torch.empty_like(src)
     lay = zero.zero_layout([n], 1, 0, 1)
     ptrs = zero.pointer_array([dst])
@@ -471,13 +499,15 @@ def main():
     args = parse()
     if args.pmc_summary:
         from fsdp_sharded_mixed_zero_amd import synth
+        if args.accum > 1 or args.separate_norm or args.flat:
+            sys.exit("counters are summarised for the default mode or --separate-unpack")
         print(json.dumps(pmc_summary(*args.pmc_summary, synth.WORKLOADS[args.workload], args.steps,
-                                     args.warmup, args.accum, args.separate_norm), indent=1))
+                                     args.warmup, args.separate_unpack), indent=1))
         return
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth
         print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup,
-                            args.accum, args.separate_norm, args.flat), end="")
+                            args.accum, args.separate_norm, args.flat, args.separate_unpack), end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -504,7 +534,8 @@ def main():
     torch.cuda.set_device(0)
     if args.offload:
         return offload_main(args, wl)
-    rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum, flat=args.flat)
+    rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum, flat=args.flat,
+                   fused_unpack=not args.separate_unpack)
     torch.cuda.synchronize()
 
     t = wl.step
@@ -557,8 +588,9 @@ def main():
     launch_bytes = algo["adamw"] / adamw_launches
     achieved = launch_bytes / (adamw_launch_ms * 1e-3) / 1e9
     step_bytes = sum(algo.values())
-    default_kernel = rs.bucket <= 0 and args.accum == 1
-    traffic = measured_traffic(wl.name, "adamw_vec_kernel<unsigned short>") if default_kernel else None
+    default_kernel = rs.bucket <= 0 and args.accum == 1 and not args.flat
+    traffic = (measured_traffic(wl.name, update_kernel(args.accum, args.separate_unpack, args.flat))
+               if default_kernel else None)
 
     out = {
         "metric": "fused sharded AdamW params/sec/GPU + achieved HBM GB/s (% of MI355X peak)",
@@ -575,11 +607,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name} rank {rs.rank} of N_d={wl.n_d}: one rank's shard, " + (
                                "ZeRO-1 flat buffers: sum of squares -> clip+AdamW+bf16 cast on the rank's slice"
-                               if args.flat else "pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack"),
+                               if args.flat else
+                               "pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack" if args.separate_unpack
+                               else "pack + sum of squares -> clip+AdamW+bf16 cast with the unpack fused"),
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
                    "segments_in_shard": len(rs.segments), "adamw_step": wl.step,
                    "bucket": rs.bucket,
                    "norm": "separate" if args.separate_norm or args.flat else "fused into pack",
+                   "unpack": ("none (flat buffers)" if args.flat else
+                              "separate" if args.separate_unpack else "fused into AdamW"),
                    "fp32_grad_accumulation_micro_batches": args.accum if args.accum > 1 else None},
         "adamw_params_per_s": launch_elems / (adamw_launch_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -595,7 +631,7 @@ def main():
     del rs
     torch.cuda.empty_cache()
     if not args.no_copy_ceiling:
-        out["copy_ceiling"] = copy_ceiling(torch, min(int(launch_bytes), 8 << 30))
+        out["copy_ceiling"] = copy_ceiling(torch, ceiling_elems(launch_bytes))
     out.update(baselines)
     print(json.dumps(out), flush=True)
 

@@ -653,12 +653,15 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_elem_kernel(const AdamWArg
 constexpr int kUnpackMaxPieces = 64;
 constexpr int kWave = 64;
 
+constexpr int kUnpackSlots = 256;
+
 struct UnpackPieces {
   int32_t n;                               // pieces (0: no tensor element in the range)
-  int32_t _pad;
+  int32_t slot_shift;                      // element lo[0] + j lies in slot j >> slot_shift
   uint64_t vec_mask;                       // bit p: 4-element stores to piece p are 8-byte aligned
   int64_t lo[kUnpackMaxPieces + 1];        // piece p holds shard elements [lo[p], lo[p+1]); lo[n] ends the last
   uint16_t* dst[kUnpackMaxPieces];         // tensor element of shard element lo[p]
+  uint8_t slot_piece[kUnpackSlots];        // piece holding each slot's first element
 };
 static_assert(sizeof(AdamWArgs) + sizeof(UnpackPieces) <= 4096, "kernel arguments fit the 4 KiB segment");
 
@@ -669,20 +672,20 @@ __device__ __forceinline__ int64_t wave_first(int64_t x) {
   return int64_t((uint64_t(hi) << 32) | lo);
 }
 
-// The piece holding shard element e (uniform; lo[0] <= e): the last p with lo[p] <= e.
+// The piece holding shard element e (uniform; lo[0] <= e < lo[n]): the last p
+// with lo[p] <= e, from the slot table and a short forward step (a binary
+// search is a chain of dependent scalar loads at the start of every wave).
 __device__ __forceinline__ int unpack_piece(const UnpackPieces& U, int64_t e) {
-  int lo = 0, hi = U.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (U.lo[mid] <= e) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+  int p = U.slot_piece[(e - U.lo[0]) >> U.slot_shift];
+  while (U.lo[p + 1] <= e) ++p;
+  return p;
 }
 
 // Store the bf16 values of this lane's shard elements [e, e + N) (N = 1 or 4;
 // for 4, packed in two words) at their tensor positions. The active lanes of
 // the wave hold consecutive elements starting at the first active lane's, all
-// within W elements of it.
+// within W elements of it. (Looking the destination up before the update's
+// loads, to overlap its scalar loads with them, measured slower.)
 template <int N, int W>
 __device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, uint32_t w0, uint32_t w1) {
   if (U.n == 0) return;
@@ -1061,6 +1064,17 @@ static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_para
       if (((uintptr_t(pieces[i].dst) - 2 * uintptr_t(lo)) & 7u) == 0) U.vec_mask |= uint64_t(1) << n;
     }
     U.n = n;
+    if (n > 0) {   // slot table over [lo[0], lo[n]): the smallest power-of-two slot that needs <= 256 slots
+      const int64_t span = U.lo[n] - U.lo[0];
+      int shift = 0;
+      while (((span + (int64_t(1) << shift) - 1) >> shift) > kUnpackSlots) ++shift;
+      U.slot_shift = shift;
+      for (int q = 0, slot = 0; slot < kUnpackSlots; ++slot) {
+        const int64_t first = U.lo[0] + (int64_t(slot) << shift);
+        while (q + 1 < n && U.lo[q + 1] <= first) ++q;
+        U.slot_piece[slot] = uint8_t(q);
+      }
+    }
     const int64_t r1 = i < pieces.size() ? U.lo[n] : end;
     const unsigned blocks = adamw_range(&a, r0, r1, vec);
     if (vec)

@@ -15,7 +15,9 @@ hold them), the flat bf16 gradient and parameter shards, the fp32 state
 (master, m, v: one 12 B/element buffer in the library's tiled layout), the
 ranks' partial sums and the sum-of-squares workspace. With ``bucket`` > 0
 the shard is processed in pieces of that many elements, a constant-size
-working set (notes, section 5.2). With ``accum_steps`` = K > 1 the step runs
+working set (notes, section 5.2). By default the unpack is fused into the
+update (zero_adamw_step_unpack: AdamW also stores each bf16 parameter at its
+tensor position); ``fused_unpack=False`` runs it as its own pass. With ``accum_steps`` = K > 1 the step runs
 K micro-batches of pack + fp32 accumulation, then the norm and AdamW on the
 fp32 accumulator ("第 5 课：ZeRO 与 FSDP" section 2, fp32 gradient
 accumulation, 4 extra bytes per shard element).
@@ -38,7 +40,7 @@ from . import synth, zero
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
                  fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
-                 accum_steps: int = 1, flat: bool = False):
+                 accum_steps: int = 1, flat: bool = False, fused_unpack: bool = True):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -83,6 +85,7 @@ class RankShard:
         self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
         self.fused_norm = fused_norm
+        self.fused_unpack = fused_unpack and not flat
         self.accum_steps = accum_steps
         self.acc = torch.empty(S, dtype=torch.float32, device=dev) if accum_steps > 1 else None
         ws = max(max(zero.zero_sqnorm_workspace_bytes(n),
@@ -191,6 +194,11 @@ class RankShard:
             mark("sqnorm", lambda: zero.zero_shard_sqnorm(self.grad_shard[b:], n, own, k > 0,
                                                           self.workspace, stream=stream))
         for b, n in pieces:
+            if self.fused_unpack:
+                mark("adamw", lambda: zero.zero_adamw_step_unpack(
+                    self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                    self.wl.n_d, self.layout, self.param_ptrs, stream))
+                continue
             mark("adamw", lambda: zero.zero_adamw_step(
                 self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
                 self.wl.n_d, stream))
@@ -219,6 +227,11 @@ class RankShard:
             mark("sqnorm", lambda: zero.zero_shard_sqnorm_f32(self.acc[b:], n, own, k > 0, self.workspace,
                                                               stream=stream))
         for b, n in pieces:
+            if self.fused_unpack:
+                mark("adamw", lambda: zero.zero_adamw_step_f32grad_unpack(
+                    self.acc, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                    self.wl.n_d, self.layout, self.param_ptrs, stream))
+                continue
             mark("adamw", lambda: zero.zero_adamw_step_f32grad(
                 self.acc, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
                 self.wl.n_d, stream))
@@ -231,7 +244,9 @@ class RankShard:
         writes only 2 on padding, unpack moves nothing there). Accumulating K
         micro-batches: K packs, accumulation 6 then 10 bytes per element, an
         fp32 norm (4) and AdamW on fp32 gradients (30). Flat buffers: the sum
-        of squares (2) and AdamW (28) only."""
+        of squares (2) and AdamW (28) only. With the unpack fused into AdamW,
+        AdamW also writes 2 bytes per real element to the tensors and there is
+        no unpack pass."""
         if self.flat:
             return {"sqnorm": 2 * self.shard, "adamw": 28 * self.shard}
         pad = self.shard - self.real
@@ -239,13 +254,18 @@ class RankShard:
         if self.accum_steps > 1:
             K, S = self.accum_steps, self.shard
             # accumulate: 2 + 4 bytes for the first micro-batch, 2 + 4 + 4 after
-            return {"pack": K * pack, "accumulate": 6 * S + (K - 1) * 10 * S, "sqnorm": 4 * S,
-                    "adamw": 30 * S, "unpack": 4 * self.real}
-        out = {"adamw": 28 * self.shard, "unpack": 4 * self.real}
-        if self.fused_norm:
-            out["pack_sqnorm"] = pack
+            out = {"pack": K * pack, "accumulate": 6 * S + (K - 1) * 10 * S, "sqnorm": 4 * S,
+                   "adamw": 30 * S}
         else:
-            out.update(pack=pack, sqnorm=2 * self.shard)
+            out = {"adamw": 28 * self.shard}
+            if self.fused_norm:
+                out["pack_sqnorm"] = pack
+            else:
+                out.update(pack=pack, sqnorm=2 * self.shard)
+        if self.fused_unpack:
+            out["adamw"] += 2 * self.real
+        else:
+            out["unpack"] = 4 * self.real
         return out
 
 
@@ -272,7 +292,8 @@ class OffloadRank(RankShard):
         import numpy as np
         import os
 
-        super().__init__(wl, rank, device, fill=fill, bucket=wl.bucket or bucket, fused_norm=True)
+        super().__init__(wl, rank, device, fill=fill, bucket=wl.bucket or bucket, fused_norm=True,
+                         fused_unpack=False)
         S = self.shard
         self.h_state = np.empty(3 * S, np.float32)
         if fill:

@@ -41,12 +41,21 @@ def test_algorithmic_bytes_modes():
     S = 262_144
     s, real, b = bench.algorithmic_bytes(wl)
     assert (s, real) == (S, S)
+    # default: the norm fused into pack, the unpack fused into AdamW (2 more bytes)
+    assert b == {"copy_pieces_kernel<true>": 4 * S, "adamw_unpack_vec_kernel<unsigned short>": 30 * S}
+    _, _, b = bench.algorithmic_bytes(wl, separate_unpack=True)
     assert b == {"copy_pieces_kernel<false>": 4 * S, "copy_pieces_kernel<true>": 4 * S,
                  "adamw_vec_kernel<unsigned short>": 28 * S}
-    _, _, b = bench.algorithmic_bytes(wl, separate_norm=True)
+    _, _, b = bench.algorithmic_bytes(wl, separate_norm=True, separate_unpack=True)
     assert b == {"copy_pieces_kernel<false>": 8 * S, "sqnorm_partial_kernel": 2 * S,
                  "adamw_vec_kernel<unsigned short>": 28 * S}
+    _, _, b = bench.algorithmic_bytes(wl, separate_norm=True)
+    assert b == {"copy_pieces_kernel<false>": 4 * S, "sqnorm_partial_kernel": 2 * S,
+                 "adamw_unpack_vec_kernel<unsigned short>": 30 * S}
     _, _, b = bench.algorithmic_bytes(wl, accum=4)
+    assert b == {"copy_pieces_kernel<false>": 4 * 4 * S, "accumulate_kernel": (6 + 30) * S,
+                 "sqnorm_f32_partial_kernel": 4 * S, "adamw_unpack_vec_kernel<float>": 32 * S}
+    _, _, b = bench.algorithmic_bytes(wl, accum=4, separate_unpack=True)
     assert b == {"copy_pieces_kernel<false>": 4 * S + 4 * 4 * S, "accumulate_kernel": (6 + 30) * S,
                  "sqnorm_f32_partial_kernel": 4 * S, "adamw_vec_kernel<float>": 30 * S}
     _, _, b = bench.algorithmic_bytes(wl, flat=True)
@@ -61,6 +70,8 @@ def test_algorithmic_bytes_with_padding():
     S, real, b = bench.algorithmic_bytes(wl)
     assert S - real == 7_488
     assert b["copy_pieces_kernel<true>"] == 4 * real + 2 * (S - real)
+    assert b["adamw_unpack_vec_kernel<unsigned short>"] == 28 * S + 2 * real   # no tensor writes on padding
+    _, _, b = bench.algorithmic_bytes(wl, separate_unpack=True)
     assert b["copy_pieces_kernel<false>"] == 4 * real
     assert b["adamw_vec_kernel<unsigned short>"] == 28 * S
 
@@ -89,8 +100,8 @@ def test_stats_summary_table(tmp_path):
             {"Name": names["final"], "Calls": 12, "AverageNs": 3000, "MinNs": 2900, "MaxNs": 3100}]
     _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_stats.csv"),
                ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"], rows)
-    md = bench.stats_summary(str(tmp_path / "prof"), wl, steps=10, warmup=2)
-    assert "--steps 10 --warmup 2 --no-cpu-baseline --no-copy-ceiling" in md
+    md = bench.stats_summary(str(tmp_path / "prof"), wl, steps=10, warmup=2, separate_unpack=True)
+    assert "--steps 10 --warmup 2 --separate-unpack --no-cpu-baseline --no-copy-ceiling" in md
     assert "12 steps traced" in md
     table = {line.split("|")[1].strip(): [c.strip() for c in line.split("|")[2:-1]]
              for line in md.splitlines() if line.startswith("| ") and not line.startswith("| kernel |")}
@@ -103,21 +114,49 @@ def test_stats_summary_table(tmp_path):
     assert table["sqnorm_final_kernel"][5] == "-"
 
 
-@needs_lib
-def test_pmc_summary_calibration(tmp_path):
-    """FETCH_SIZE reading half the bytes and WRITE_SIZE all of them (as
-    measured on MI355X): the copy kernel calibrates factors 2 and 1, and a
-    kernel whose raw counters match its algorithmic bytes comes out at 1.0."""
-    wl = synth.WORKLOADS["tiny"]
-    S = 262_144
-    copy, adamw = "copy_pieces_kernel<false>", "adamw_vec_kernel<unsigned short>"
-    raw = {copy: (2 * S / 1024 / 2, 2 * S / 1024), adamw: (14 * S / 1024 / 2, 14 * S / 1024 * 1.01)}
+def _counter_csvs(tmp_path, raw):
+    raw = dict(raw, sqnorm_final_kernel=(1.0, 0.0))     # once per step: the trace's step count
     for counter, k in (("FETCH_SIZE", 0), ("WRITE_SIZE", 1)):
         rows = [{"Kernel_Name": f"void (anonymous namespace)::{name}(x)", "Counter_Name": counter,
                  "Counter_Value": vals[k]} for name, vals in raw.items() for _ in range(5)]
         _write_csv(str(tmp_path / counter / "y" / "bench_counter_collection.csv"),
                    ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
-    out = bench.pmc_summary(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), wl, steps=3, warmup=2)
+    return str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE")
+
+
+@needs_lib
+def test_pmc_summary_calibration_from_the_copy_ceiling(tmp_path):
+    """Default mode: the copy ceiling's plain copy (4 bytes per element of its
+    buffers, sized from the update's bytes per launch) calibrates the
+    counters; FETCH_SIZE reading half the bytes and WRITE_SIZE all of them (as
+    measured on MI355X) give factors 2 and 1, and the fused update whose raw
+    counters match its 30 bytes per element comes out at 1.0."""
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    copy, update = "copy_pieces_kernel<false>", "adamw_unpack_vec_kernel<unsigned short>"
+    n = bench.ceiling_elems(30 * S)
+    assert n == 30 * S // 4
+    raw = {copy: (2 * n / 1024 / 2, 2 * n / 1024), update: (14 * S / 1024 / 2, 16 * S / 1024),
+           "copy_pieces_kernel<true>": (2 * S / 1024 / 2, 2 * S / 1024)}
+    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw), wl, steps=3, warmup=2)
+    assert out["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert out["calibration"]["write_factor"] == pytest.approx(1.0)
+    assert out["kernels"][update]["algorithmic_bytes"] == 30 * S
+    assert out["kernels"][update]["traffic_over_algorithmic"] == pytest.approx(1.0)
+    assert out["kernels"]["copy_pieces_kernel<true>"]["traffic_over_algorithmic"] == pytest.approx(1.0)
+    assert "--no-copy-ceiling" not in out["commands"][0]
+
+
+@needs_lib
+def test_pmc_summary_calibration(tmp_path):
+    """--separate-unpack: the unpack calibrates the counters (factors 2 and
+    1), and a kernel whose raw counters match its algorithmic bytes comes out
+    at 1.0."""
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    copy, adamw = "copy_pieces_kernel<false>", "adamw_vec_kernel<unsigned short>"
+    raw = {copy: (2 * S / 1024 / 2, 2 * S / 1024), adamw: (14 * S / 1024 / 2, 14 * S / 1024 * 1.01)}
+    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw), wl, steps=3, warmup=2, separate_unpack=True)
     assert out["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert out["calibration"]["write_factor"] == pytest.approx(1.0)
     assert out["kernels"][copy]["traffic_over_algorithmic"] == pytest.approx(1.0)

@@ -34,7 +34,10 @@ def test_bench_json_line():
     roof = d["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["achieved"] > 0 and roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
-    assert roof["algorithmic_bytes_per_launch"] == 28 * d["config"]["shard_params"]
+    S = d["config"]["shard_params"]
+    fused = d["config"]["unpack"] == "fused into AdamW"
+    assert fused                                   # the default path
+    assert roof["algorithmic_bytes_per_launch"] == 28 * S + 2 * S    # the tiny shard has no padding
     parallel = len(os.sched_getaffinity(0)) > 1
     for base in ("cpu_baseline", "cpu_baseline_parallel") if parallel else ("cpu_baseline",):
         b = d[base]

@@ -78,19 +78,20 @@ def oracle_partial(grad_shard, S):
     return total
 
 
-# (workload, fused norm, bucket): None keeps the workload's own bucketing. The
-# 70B shard in one piece makes a single AdamW launch of 2.2e9 four-element
-# units, more than its 2^23-block grid holds, so that launch strides; the
-# fused pack then covers 8.6e9 elements in two launches and its final sum
-# adds ~1e6 block partials.
-FULL_SIZE = ([(n, f, None) for n in ("gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b") for f in (True, False)]
-             + [("llama-70b", True, 0)])
+# (workload, fused norm, bucket, fused unpack): bucket None keeps the
+# workload's own bucketing. The 70B shard in one piece makes a single AdamW
+# launch of 2.2e9 four-element units, more than its 2^23-block grid holds, so
+# that launch strides; the fused pack then covers 8.6e9 elements in two
+# launches and its final sum adds ~1e6 block partials. The 7B shard's 75
+# segments take two launches of the fused update.
+FULL_SIZE = ([(n, f, None, True) for n in ("gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b") for f in (True, False)]
+             + [("llama-70b", True, 0, True), ("gpt-7.5b", True, None, False), ("llama-7b", True, None, False)])
 
 
-@pytest.mark.parametrize("name,fused_norm,bucket", FULL_SIZE,
+@pytest.mark.parametrize("name,fused_norm,bucket,fused_unpack", FULL_SIZE,
                          ids=[f"{n}-{'fused' if f else 'separate'}-norm{'-one-piece' if b == 0 else ''}"
-                              for n, f, b in FULL_SIZE])
-def test_workload_full_size(name, fused_norm, bucket):
+                              f"{'' if u else '-separate-unpack'}" for n, f, b, u in FULL_SIZE])
+def test_workload_full_size(name, fused_norm, bucket, fused_unpack):
     import dataclasses
 
     from fsdp_sharded_mixed_zero_amd.rank import RankShard
@@ -105,7 +106,7 @@ def test_workload_full_size(name, fused_norm, bucket):
     print(f"\n[{name}] shard {S}, {len(lay.segments)} segments, bucket {wl.bucket}, "
           f"{len(ranges)} sampled ranges, fused norm {fused_norm}", flush=True)
 
-    rs = RankShard(wl, fill=False, fused_norm=fused_norm)
+    rs = RankShard(wl, fill=False, fused_norm=fused_norm, fused_unpack=fused_unpack)
     assert rs.shard == S
     assert rs.segments == [(s.tensor, s.src_off, s.dst_off, s.length) for s in lay.segments]
     before = {}
