@@ -687,11 +687,14 @@ __device__ __forceinline__ int unpack_piece(const UnpackPieces& U, int64_t e) {
 // within W elements of it. (Looking the destination up before the update's
 // loads, to overlap its scalar loads with them, measured slower.)
 template <int N, int W>
-__device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, uint32_t w0, uint32_t w1) {
+__device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, uint32_t w0, uint32_t w1,
+                                            int hint = -1) {
   if (U.n == 0) return;
   const int64_t w_lo = wave_first(e);
   if (w_lo >= U.lo[U.n]) return;                     // padding only
-  int p = w_lo < U.lo[0] ? 0 : unpack_piece(U, w_lo);
+  // `hint`: the piece of the block's first element, looked up at the start
+  int p = hint >= 0 && w_lo >= U.lo[hint] && w_lo + W <= U.lo[hint + 1] ? hint
+          : w_lo < U.lo[0] ? 0 : unpack_piece(U, w_lo);
   if (w_lo >= U.lo[p] && w_lo + W <= U.lo[p + 1]) {  // the whole wave lies in piece p
     uint16_t* d = U.dst[p] + (e - U.lo[p]);
     if constexpr (N == 4) {
@@ -721,6 +724,10 @@ __device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, ui
 
 template <typename G>
 __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const AdamWArgs a, const UnpackPieces U) {
+  // the piece of this block's first element (first pass of the loop), from
+  // the block index alone: its scalar loads start before any data is loaded
+  const int64_t b_lo = (a.u_begin + int64_t(blockIdx.x) * kAdamThreads) << 2;
+  const int hint = U.n > 0 && b_lo >= U.lo[0] && b_lo < U.lo[U.n] ? unpack_piece(U, b_lo) : -1;
   const float c = clip_coefficient(a);
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
   for (int64_t u = a.u_begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < a.u_end; u += stride) {
@@ -748,7 +755,7 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const Ad
     __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, vs);
     const uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
     __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(a.param + e));
-    unpack_lane<4, 4 * kWave>(U, e, w0, w1);
+    unpack_lane<4, 4 * kWave>(U, e, w0, w1, hint);
   }
   // up to 3 elements before the first unit and after the last one
   if (blockIdx.x == 0) {
