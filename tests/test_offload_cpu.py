@@ -127,3 +127,18 @@ def test_cpu_adamw_in_forked_child():
             os._exit(code)
     _, status = os.waitpid(pid, 0)
     assert os.WIFEXITED(status) and os.WEXITSTATUS(status) == 0
+
+
+@pytest.mark.parametrize("kind", ["moments", "decay"])
+def test_cpu_adamw_keeps_subnormals(kind):
+    """Subnormal gradients, moments and master weights go through the host
+    update unflushed, as in the oracle."""
+    import denormal_inputs as D
+    n = 3 * TILE + 7
+    bits, master, m, v, ohp, step, parts = D.case(kind, n, seed=41)
+    state = to_tiles(master, m, v)
+    param = np.zeros(n, np.uint16)
+    zero.zero_cpu_adamw_step(bits, state, param, n, 0, n, _hp(ohp, step), parts, parts.size, 3)
+    coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
+    want = O.adamw_step(bits, master, m, v, step, ohp, coef)
+    D.check_against_oracle((*from_tiles(state, n), param), want, m, v)
