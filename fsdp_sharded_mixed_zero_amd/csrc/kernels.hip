@@ -480,6 +480,12 @@ __global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const dou
 
 constexpr int kAdamThreads = 256;
 constexpr int64_t kAdamMaxBlocks = int64_t(1) << 23;   // 2^31 work-items
+// A range longer than this is updated in several launches of equal length
+// (rounded up to whole tiles). Measured on MI355X over a 1.68 G-element state:
+// one launch 7.41 ms, launches of 2^27 or 2^26 elements 7.29-7.30 ms, of 2^25
+// 7.33 ms; at 119 M elements one launch and two take the same time. (The copy
+// kernels are fastest as one launch: each cut costs them ~3 us.)
+constexpr int64_t kAdamLaunchElems = int64_t(1) << 27;
 constexpr int kTileLog2 = 13;
 constexpr int64_t kTile = int64_t(1) << kTileLog2;     // ZERO_STATE_TILE
 static_assert(kTile == ZERO_STATE_TILE, "state tile size");
@@ -1003,6 +1009,15 @@ static int adamw_args(const G* d_grad, float* d_state, uint16_t* d_param, int64_
   return zero::ok();
 }
 
+// Elements per launch for a range of `count`: the fewest launches of at most
+// kAdamLaunchElems, of equal length rounded up to whole tiles.
+static int64_t adamw_chunk(int64_t count) {
+  if (count <= 0) return kTile;
+  const int64_t k = (count + kAdamLaunchElems - 1) / kAdamLaunchElems;
+  const int64_t c = (count + k - 1) / k;
+  return (c + kTile - 1) / kTile * kTile;
+}
+
 // Sets a's range to [r0, r1) and returns the grid for it.
 static unsigned adamw_range(AdamWArgs* a, int64_t r0, int64_t r1, bool vec) {
   a->begin = r0;
@@ -1025,19 +1040,25 @@ static int adamw_launch(const G* d_grad, float* d_state, uint16_t* d_param, int6
                           &vec))
     return rc;
   if (count == 0) return zero::ok();
-  const unsigned blocks = adamw_range(&a, begin, begin + count, vec);
-  if (vec)
-    hipLaunchKernelGGL(adamw_vec_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(adamw_elem_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  const int64_t end = begin + count, chunk = adamw_chunk(count);
+  for (int64_t r0 = begin; r0 < end;) {
+    const int64_t r1 = std::min(end, r0 + chunk);
+    const unsigned blocks = adamw_range(&a, r0, r1, vec);
+    if (vec)
+      hipLaunchKernelGGL(adamw_vec_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(adamw_elem_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    r0 = r1;
+  }
   return zero::ok();
 }
 
-// The update with the unpack fused: one launch per run of up to
-// kUnpackMaxPieces pieces of the range; the last launch also covers the
-// padding after the last piece.
+// The update with the unpack fused: launches of adamw_chunk(count) elements
+// at most and kUnpackMaxPieces pieces, a piece cut by a launch boundary
+// continuing in the next launch; the last launch also covers the padding
+// after the last piece.
 template <typename G>
 static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
                                int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms,
@@ -1055,22 +1076,27 @@ static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_para
   if (count == 0) return zero::ok();
   std::vector<Piece> pieces;
   if (int rc = build_pieces(h, tensor_params, d_param, begin, count, false, &pieces, who)) return rc;
-  const int64_t end = begin + count;
-  size_t i = 0;
-  int64_t r0 = begin;
-  do {
+  const int64_t end = begin + count, chunk = adamw_chunk(count);
+  size_t i = 0;                  // the first piece not finished by earlier launches
+  for (int64_t r0 = begin; r0 < end;) {
+    int64_t r1 = std::min(end, r0 + chunk);
     UnpackPieces U{};
     int n = 0;
-    for (; i < pieces.size() && n < kUnpackMaxPieces; ++i, ++n) {
-      const int64_t lo = pieces[i].src - d_param;            // the piece's first shard element
+    size_t j = i;
+    for (; j < pieces.size() && n < kUnpackMaxPieces; ++j, ++n) {
+      const int64_t plo = pieces[j].src - d_param;           // the piece's first shard element
+      if (plo >= r1) break;
+      const int64_t lo = std::max(plo, r0);
       if (lo != (n == 0 ? r0 : U.lo[n]))
         return fail(ZERO_EINVAL, "%s: internal error: pieces not contiguous at element %lld", who, (long long)lo);
       U.lo[n] = lo;
-      U.lo[n + 1] = lo + pieces[i].len;
-      U.dst[n] = pieces[i].dst;
-      if (((uintptr_t(pieces[i].dst) - 2 * uintptr_t(lo)) & 7u) == 0) U.vec_mask |= uint64_t(1) << n;
+      U.lo[n + 1] = std::min(plo + pieces[j].len, r1);
+      U.dst[n] = pieces[j].dst + (lo - plo);
+      if (((uintptr_t(U.dst[n]) - 2 * uintptr_t(lo)) & 7u) == 0) U.vec_mask |= uint64_t(1) << n;
     }
     U.n = n;
+    // a full table with pieces still starting inside the launch: end it at its last piece
+    if (n == kUnpackMaxPieces && j < pieces.size() && pieces[j].src - d_param < r1) r1 = U.lo[n];
     if (n > 0) {   // slot table over [lo[0], lo[n]): the smallest power-of-two slot that needs <= 256 slots
       const int64_t span = U.lo[n] - U.lo[0];
       int shift = 0;
@@ -1082,7 +1108,6 @@ static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_para
         U.slot_piece[slot] = uint8_t(q);
       }
     }
-    const int64_t r1 = i < pieces.size() ? U.lo[n] : end;
     const unsigned blocks = adamw_range(&a, r0, r1, vec);
     if (vec)
       hipLaunchKernelGGL(adamw_unpack_vec_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a, U);
@@ -1090,8 +1115,9 @@ static int adamw_unpack_launch(const G* d_grad, float* d_state, uint16_t* d_para
       hipLaunchKernelGGL(adamw_unpack_elem_kernel<G>, dim3(blocks), dim3(kAdamThreads), 0, stream, a, U);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    while (i < pieces.size() && pieces[i].src - d_param + pieces[i].len <= r1) ++i;
     r0 = r1;
-  } while (i < pieces.size());
+  }
   return zero::ok();
 }
 

@@ -155,6 +155,24 @@ def test_device_calls_reject_bad_arguments_on_the_host():
         assert fn(None, None, None, 128, 3, 0, ctypes.byref(off), None, 0, lay.handle, arr, None) == zero.ZERO_OK
 
 
+def test_empty_ranges_return_before_any_launch():
+    """An update over an empty range is a no-op that returns OK on the host
+    (no launch, no division by its length), at the start, inside and at the
+    end of the state, with clipping on and off."""
+    lib = zero.library()
+    lay = zero.zero_layout([100, 28], 1, 0, 1)
+    arr = (ctypes.c_void_p * 2)()
+    parts = ctypes.c_void_p(8)            # never read: nothing is launched
+    for hp, sq, n_ranks in ((zero.hparams(max_norm=0.0, step=1), None, 0),
+                            (zero.hparams(max_norm=1.0, step=3), parts, 4)):
+        for begin in (0, 5, 128):
+            for fn in (lib.zero_adamw_step, lib.zero_adamw_step_f32grad):
+                assert fn(None, None, None, 128, begin, 0, ctypes.byref(hp), sq, n_ranks, None) == zero.ZERO_OK
+            for fn in (lib.zero_adamw_step_unpack, lib.zero_adamw_step_f32grad_unpack):
+                assert fn(None, None, None, 128, begin, 0, ctypes.byref(hp), sq, n_ranks, lay.handle, arr,
+                          None) == zero.ZERO_OK
+
+
 def test_state_tile_constant_matches_header():
     from state_tiles import TILE
     assert TILE == zero.ZERO_STATE_TILE
