@@ -234,7 +234,9 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
  *   d_rank_sqnorms  device array of n_ranks doubles (the ranks' partial sums
  *             of squares in rank order); may be NULL when max_norm <= 0
  * Pointers with d_grad/d_param 8-byte and d_state 16-byte alignment take the
- * vector path, others a slower element path with identical results.
+ * vector path, others a slower element path with identical results. A range
+ * longer than 2^27 elements is updated in several equal launches on `stream`
+ * (each element once; the results do not depend on the split).
  * Errors: ZERO_EINVAL for null pointers (all may be NULL when count == 0), a
  * range outside [0, n_state), step < 1, n_ranks < 1 with clipping on;
  * ZERO_EHIP if a launch fails. Non-finite inputs propagate per IEEE rules (a
@@ -255,8 +257,8 @@ int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, i
  *   tensor_params  HOST array of the layout's n_tensors device pointers to the
  *                  per-tensor bf16 parameters (as zero_unpack_params)
  * Results are bit-identical to the two calls. Padding elements update state
- * and the shard only. Ranges touching more than 64 tensor pieces take more
- * than one launch.
+ * and the shard only. Ranges touching more than 64 tensor pieces, or longer
+ * than 2^27 elements, take more than one launch (all on `stream`).
  * Errors: as zero_adamw_step and zero_unpack_params, plus ZERO_EINVAL when
  * n_state differs from the layout's shard size. */
 int zero_adamw_step_unpack(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,
