@@ -1,19 +1,26 @@
 // Device code and device-side C ABI of libzero_mi355x.so (gfx950 / CDNA4).
 //
-// All four kernels stream HBM; none is a dense contraction, so none uses the
-// matrix cores. They are written for 64-lane wavefronts and one rule measured
-// on MI355X: every wavefront-wide memory instruction covers one contiguous
-// span (lane k takes the k-th 8 or 16 bytes), and the grid is one-shot (one
-// unit of work per lane, blocks dispatched in address order), so the waves in
-// flight at any moment touch a compact window of each stream. Persistent
-// grid-stride loops and lanes that own 32 contiguous bytes (two half-filled
-// instructions per stream) both measured 10-20% slower. Loads and stores are
-// non-temporal: nothing is reused within a step.
+// Every kernel here streams HBM; none is a dense contraction, so none uses
+// the matrix cores. They are written for 64-lane wavefronts and one rule
+// measured on MI355X: every wavefront-wide memory instruction covers one
+// contiguous span (lane k takes the k-th 8 or 16 bytes), and the grid is
+// one-shot (one unit of work per lane, blocks dispatched in address order),
+// so the waves in flight at any moment touch a compact window of each stream.
+// Persistent grid-stride loops and lanes that own 32 contiguous bytes (two
+// half-filled instructions per stream) both measured 10-20% slower. Loads and
+// stores are non-temporal: nothing is reused within a step.
 //
-//   copy_pieces_kernel   pack (tensors -> shard) and unpack (shard -> tensors)
-//   sqnorm_partial_kernel / sqnorm_final_kernel
-//                        deterministic two-stage sum of squares (fp64)
-//   adamw_kernel         clip + AdamW + bf16 cast, 28 bytes per element
+//   copy_pieces_kernel<SQ>    pack (tensors -> shard) and unpack (shard ->
+//                             tensors); with SQ the pack also sums squares
+//   sqnorm_partial_kernel, sqnorm_f32_partial_kernel, sqnorm_final_kernel
+//                             deterministic two-stage sum of squares (fp64)
+//   adamw_vec_kernel, adamw_elem_kernel
+//                             clip + AdamW + bf16 cast, 28 bytes per element
+//   adamw_unpack_vec_kernel, adamw_unpack_elem_kernel
+//                             the same, also storing each bf16 parameter at its
+//                             tensor position (30 bytes per element)
+//   accumulate_kernel         fp32 gradient accumulation over micro-batches
+//   state_convert_kernel      three fp32 arrays <-> the tiled state buffer
 //
 // Sources for what is computed: "第 5 课：ZeRO 与 FSDP" sections 2-3, notes on
 // "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
@@ -731,7 +738,11 @@ __device__ __forceinline__ void unpack_lane(const UnpackPieces& U, int64_t e, ui
 template <typename G>
 __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const AdamWArgs a, const UnpackPieces U) {
   // the piece of this block's first element (first pass of the loop), from
-  // the block index alone: its scalar loads start before any data is loaded
+  // the block index alone: its scalar loads start before any data is loaded.
+  // (Issuing the lane's first loads before the clip coefficient, which every
+  // wave forms in a chain of dependent loads and adds, measured 559-563 us at
+  // the 7.5B shard against 559-560 us as written: that chain is not what
+  // limits the stream.)
   const int64_t b_lo = (a.u_begin + int64_t(blockIdx.x) * kAdamThreads) << 2;
   const int hint = U.n > 0 && b_lo >= U.lo[0] && b_lo < U.lo[U.n] ? unpack_piece(U, b_lo) : -1;
   const float c = clip_coefficient(a);
@@ -964,7 +975,8 @@ extern "C" int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* 
 
 // Checks the arguments of an update over [begin, begin+count) and fills the
 // kernel arguments (range fields for the whole range). *vec: the pointers
-// allow the vector path.
+// allow the vector path. With count == 0 it returns OK after the checks
+// without filling *out: the caller has nothing to launch.
 template <typename G>
 static int adamw_args(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
                       int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms, int32_t n_ranks,
