@@ -142,3 +142,20 @@ def test_cpu_adamw_keeps_subnormals(kind):
     coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
     want = O.adamw_step(bits, master, m, v, step, ohp, coef)
     D.check_against_oracle((*from_tiles(state, n), param), want, m, v)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cpu_adamw_random_cases(seed):
+    """Seeded random sizes, sub-ranges, hyperparameters, rank counts and
+    thread counts against the oracle."""
+    rng = np.random.default_rng(500 + seed)
+    for _ in range(6):
+        n = int(rng.integers(1, 3 * TILE + 100))
+        begin = int(rng.integers(0, n + 1)) if rng.random() < 0.6 else 0
+        count = int(rng.integers(0, n - begin + 1)) if begin else n
+        betas = [(0.9, 0.999), (0.8, 0.95)][int(rng.integers(0, 2))]
+        ohp = O.AdamWHParams(lr=float(rng.choice([1e-3, 3e-4])), beta1=betas[0], beta2=betas[1],
+                             eps=float(rng.choice([1e-8, 1e-6])), weight_decay=float(rng.choice([0.0, 0.01, 0.1])),
+                             max_norm=float(rng.choice([0.0, 1.0, 1e-3])))
+        _case(n, begin, count, int(rng.choice([1, 2, 10, 1000])), ohp, int(rng.integers(1, 200)),
+              int(rng.integers(0, 9)), seed=int(rng.integers(0, 1 << 30)))
