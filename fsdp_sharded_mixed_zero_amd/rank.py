@@ -17,10 +17,11 @@ ranks' partial sums and the sum-of-squares workspace. With ``bucket`` > 0
 the shard is processed in pieces of that many elements, a constant-size
 working set (notes, section 5.2). By default the unpack is fused into the
 update (zero_adamw_step_unpack: AdamW also stores each bf16 parameter at its
-tensor position); ``fused_unpack=False`` runs it as its own pass. With ``accum_steps`` = K > 1 the step runs
-K micro-batches of pack + fp32 accumulation, then the norm and AdamW on the
-fp32 accumulator ("第 5 课：ZeRO 与 FSDP" section 2, fp32 gradient
-accumulation, 4 extra bytes per shard element).
+tensor position); ``fused_unpack=False`` runs it as its own pass. With
+``accum_steps`` = K > 1 the step runs K micro-batches of pack + fp32
+accumulation, then the norm and AdamW on the fp32 accumulator ("第 5 课：ZeRO
+与 FSDP" section 2, fp32 gradient accumulation, 4 extra bytes per shard
+element).
 
 With ``flat=True`` the rank holds the ZeRO-1 form (notes on the ZeRO paper,
 section 4.1): the whole gradient and parameter sets live in two flat,
