@@ -161,6 +161,16 @@ def pointer_array(tensors):
     return _ptr_array(tensors)
 
 
+def _tensor_array(layout, items):
+    """The per-tensor pointer array of a call on `layout`. The library reads
+    one pointer per tensor of the layout, so a shorter array is refused here
+    (it would be read past its end)."""
+    arr = _ptr_array(items)
+    if len(arr) < layout.n_tensors:
+        raise ValueError(f"{len(arr)} tensor pointers for a layout of {layout.n_tensors} tensors")
+    return arr
+
+
 class Layout:
     """Owner of a zero_layout_t handle."""
 
@@ -216,7 +226,7 @@ def zero_layout_segments(layout: Layout):
 
 
 def zero_pack_grads(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, stream=None):
-    arr = _ptr_array(tensor_grads)
+    arr = _tensor_array(layout, tensor_grads)
     _check("zero_pack_grads", library().zero_pack_grads(
         layout.handle, arr, _ptr(grad_shard), begin, count, _stream(stream)))
 
@@ -227,7 +237,7 @@ def zero_pack_sqnorm_workspace_bytes(layout: Layout, begin: int, count: int) -> 
 
 def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, out,
                            accumulate: bool, workspace, ws_bytes: int | None = None, stream=None):
-    arr = _ptr_array(tensor_grads)
+    arr = _tensor_array(layout, tensor_grads)
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_pack_grads_sqnorm", library().zero_pack_grads_sqnorm(
@@ -236,7 +246,7 @@ def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int,
 
 
 def zero_unpack_params(layout: Layout, param_shard, tensor_params, begin: int, count: int, stream=None):
-    arr = _ptr_array(tensor_params)
+    arr = _tensor_array(layout, tensor_params)
     _check("zero_unpack_params", library().zero_unpack_params(
         layout.handle, _ptr(param_shard), arr, begin, count, _stream(stream)))
 
@@ -275,7 +285,7 @@ def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count:
 
 def zero_adamw_step_unpack(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
                            rank_sqnorms, n_ranks: int, layout: Layout, tensor_params, stream=None):
-    arr = _ptr_array(tensor_params)
+    arr = _tensor_array(layout, tensor_params)
     _check("zero_adamw_step_unpack", library().zero_adamw_step_unpack(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))
@@ -284,7 +294,7 @@ def zero_adamw_step_unpack(grad, state, param, n_state: int, begin: int, count: 
 def zero_adamw_step_f32grad_unpack(grad, state, param, n_state: int, begin: int, count: int,
                                    hp: zero_adamw_hparams, rank_sqnorms, n_ranks: int, layout: Layout,
                                    tensor_params, stream=None):
-    arr = _ptr_array(tensor_params)
+    arr = _tensor_array(layout, tensor_params)
     _check("zero_adamw_step_f32grad_unpack", library().zero_adamw_step_f32grad_unpack(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))

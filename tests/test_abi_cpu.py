@@ -210,6 +210,22 @@ def test_segments_query_with_small_capacity():
     assert lib.zero_layout_segments(lay.handle, None, 2, ctypes.byref(n)) == zero.ZERO_EINVAL
 
 
+def test_binding_refuses_short_pointer_arrays():
+    """The library reads one pointer per tensor of the layout: the binding
+    refuses a shorter array before calling it."""
+    lay = zero.zero_layout([100, 28, 5], 1, 0, 1)
+    hp = zero.hparams(step=1)
+    short = [None, None]
+    for call in (lambda: zero.zero_pack_grads(lay, short, 0, 0, 8),
+                 lambda: zero.zero_unpack_params(lay, 0, short, 0, 8),
+                 lambda: zero.zero_pack_grads_sqnorm(lay, short, 0, 0, 8, 0, False, 0, 8),
+                 lambda: zero.zero_adamw_step_unpack(0, 0, 0, 133, 0, 8, hp, 0, 1, lay, short),
+                 lambda: zero.zero_adamw_step_f32grad_unpack(0, 0, 0, 133, 0, 8, hp, 0, 1, lay,
+                                                             (ctypes.c_void_p * 2)())):
+        with pytest.raises(ValueError):
+            call()
+
+
 def test_binding_refuses_memory_on_the_wrong_side():
     """Host buffers given to a device entry point (and device buffers given to
     the host update) are refused by the binding before anything runs."""
