@@ -241,6 +241,20 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     return "\n".join(lines) + "\n"
 
 
+def single_launch_calls(rs, fused):
+    """Whether every update call of the step is one kernel launch: its range
+    is at most ZERO_ADAMW_LAUNCH_ELEMS elements and, for the update with the
+    unpack fused, touches at most ZERO_PIECES_PER_LAUNCH tensor pieces."""
+    from fsdp_sharded_mixed_zero_amd import zero
+    for b, n in rs.pieces():
+        if n > zero.ZERO_ADAMW_LAUNCH_ELEMS:
+            return False
+        touched = sum(1 for _, _, dst, length in rs.segments if dst < b + n and dst + length > b)
+        if fused and touched > zero.ZERO_PIECES_PER_LAUNCH:
+            return False
+    return True
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of ``kernel`` from the committed summary, or None
     when there is none or the kernels changed since it was taken."""
@@ -582,11 +596,14 @@ def main():
         kernels[phase] = {"us_per_step": round(per_step_ms * 1e3, 2), "launches_per_step": launches,
                           "algorithmic_bytes": algo[phase], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    adamw_launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in timing["adamw"]) / len(timing["adamw"])
-    adamw_launches = len(timing["adamw"]) / len(timed_steps)
-    launch_elems = S / adamw_launches
-    launch_bytes = algo["adamw"] / adamw_launches
-    achieved = launch_bytes / (adamw_launch_ms * 1e-3) / 1e9
+    # each event pair spans one update call: one kernel launch unless the
+    # call's range needs several (then the pair spans them all, back to back)
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in timing["adamw"]) / len(timing["adamw"])
+    calls = len(timing["adamw"]) / len(timed_steps)
+    call_elems = S / calls
+    call_bytes = algo["adamw"] / calls
+    achieved = call_bytes / (call_ms * 1e-3) / 1e9
+    single = single_launch_calls(rs, rs.fused_unpack)
     step_bytes = sum(algo.values())
     default_kernel = rs.bucket <= 0 and args.accum == 1 and not args.flat
     traffic = (measured_traffic(wl.name, update_kernel(args.accum, args.separate_unpack, args.flat))
@@ -617,21 +634,26 @@ def main():
                    "unpack": ("none (flat buffers)" if args.flat else
                               "separate" if args.separate_unpack else "fused into AdamW"),
                    "fp32_grad_accumulation_micro_batches": args.accum if args.accum > 1 else None},
-        "adamw_params_per_s": launch_elems / (adamw_launch_ms * 1e-3),
+        "adamw_params_per_s": call_elems / (call_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "kernels_note": f"per-phase times from {breakdown_steps} further steps with events around every "
                         f"phase (outside the timed region)",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(launch_bytes),
-                     "timed_launches": len(timing["adamw"]),
-                     "events": f"around the AdamW launches of every {EVENT_EVERY}th step of the timed region"},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
+    unit, units = ("launch", "launches") if single else ("call", "calls")
+    out["roofline"].update({
+        f"algorithmic_bytes_per_{unit}": int(call_bytes), f"timed_{units}": len(timing["adamw"]),
+        "events": f"around the AdamW {units} of every {EVENT_EVERY}th step of the timed region"})
+    if not single:
+        out["roofline"]["note"] = ("each update call runs as several kernel launches back to back (a range longer "
+                                   "than ZERO_ADAMW_LAUNCH_ELEMS elements or touching more than "
+                                   "ZERO_PIECES_PER_LAUNCH tensor pieces): achieved is per call")
     del rs
     torch.cuda.empty_cache()
     if not args.no_copy_ceiling:
-        out["copy_ceiling"] = copy_ceiling(torch, ceiling_elems(launch_bytes))
+        out["copy_ceiling"] = copy_ceiling(torch, ceiling_elems(call_bytes))
     out.update(baselines)
     print(json.dumps(out), flush=True)
 

@@ -104,7 +104,7 @@ __device__ __forceinline__ double block_sum(double x) {
 // table is a chain of about log2(pieces) + 1 such loads, and on waves that
 // live for one load and one store that latency costs 2-3% of the copy rate.
 
-constexpr int kCopyMaxPieces = 64;
+constexpr int kCopyMaxPieces = ZERO_PIECES_PER_LAUNCH;
 constexpr int kCopyThreads = 256;      // plain copy: one 16-byte vector per lane
 constexpr int kCopySqThreads = 512;    // copy + sum of squares: 2 vectors per lane keep more loads in flight
 constexpr int kCopyVecPerThread = 1;
@@ -492,7 +492,7 @@ constexpr int64_t kAdamMaxBlocks = int64_t(1) << 23;   // 2^31 work-items
 // one launch 7.41 ms, launches of 2^27 or 2^26 elements 7.29-7.30 ms, of 2^25
 // 7.33 ms; at 119 M elements one launch and two take the same time. (The copy
 // kernels are fastest as one launch: each cut costs them ~3 us.)
-constexpr int64_t kAdamLaunchElems = int64_t(1) << 27;
+constexpr int64_t kAdamLaunchElems = ZERO_ADAMW_LAUNCH_ELEMS;
 constexpr int kTileLog2 = 13;
 constexpr int64_t kTile = int64_t(1) << kTileLog2;     // ZERO_STATE_TILE
 static_assert(kTile == ZERO_STATE_TILE, "state tile size");
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_elem_kernel(const AdamWArg
 // congruent with the shard); a wave across a piece boundary loops over the
 // pieces it touches. Every table index is wave-uniform.
 
-constexpr int kUnpackMaxPieces = 64;
+constexpr int kUnpackMaxPieces = ZERO_PIECES_PER_LAUNCH;
 constexpr int kWave = 64;
 
 constexpr int kUnpackSlots = 256;

@@ -20,6 +20,8 @@ ZERO_EINVAL = -1
 ZERO_EHIP = -3
 ZERO_ENOMEM = -4
 ZERO_STATE_TILE = 8192      # elements per tile of the fp32 state buffer (include/zero.h)
+ZERO_PIECES_PER_LAUNCH = 64            # tensor pieces one launch carries (include/zero.h)
+ZERO_ADAMW_LAUNCH_ELEMS = 1 << 27      # longer update ranges take several launches
 
 
 class ZeroError(RuntimeError):

@@ -207,6 +207,15 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
  * arrays. */
 #define ZERO_STATE_TILE 8192
 
+/* Launch granularity of the device calls. A call's work is split into
+ * several kernel launches, one after another on the caller's stream, when
+ * its range touches more than ZERO_PIECES_PER_LAUNCH contiguous tensor pieces
+ * (pack, unpack, the fused update), or, for the updates, when the range is
+ * longer than ZERO_ADAMW_LAUNCH_ELEMS elements (then equal launches of whole
+ * tiles). Results do not depend on the split. */
+#define ZERO_PIECES_PER_LAUNCH 64
+#define ZERO_ADAMW_LAUNCH_ELEMS (1 << 27)
+
 /* ---------------------------------------------------------------------------
  * zero_adamw_step -- fused clip + AdamW + bf16 cast over shard elements
  * [begin, begin+count).

@@ -178,6 +178,15 @@ def test_state_tile_constant_matches_header():
     assert TILE == zero.ZERO_STATE_TILE
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER, encoding="utf-8").read()
+    defines = {m.group(1): eval(m.group(2), {})
+               for m in re.finditer(r"#define (ZERO_[A-Z0-9_]+)[ \t]+([^/\n]+)", text)}
+    for name in ("ZERO_OK", "ZERO_EINVAL", "ZERO_EHIP", "ZERO_ENOMEM", "ZERO_STATE_TILE",
+                 "ZERO_PIECES_PER_LAUNCH", "ZERO_ADAMW_LAUNCH_ELEMS"):
+        assert getattr(zero, name) == defines[name], name
+
+
 def test_state_tile_helper_follows_the_stated_layout():
     # element e of an n-element state: master at 3kT + j, m at 3kT + L + j,
     # v at 3kT + 2L + j (k = e // T, j = e % T, L = min(T, n - kT))

@@ -173,3 +173,26 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_single_launch_calls():
+    """Which workloads' update calls are one kernel launch (the roofline is
+    then per launch): the 7.5B shard and the 70B buckets are, the 7B shard
+    (1.68 G elements) is not, and 100 tensors in one call are not for the
+    fused update."""
+    import types
+
+    from fsdp_sharded_mixed_zero_amd import synth, zero
+
+    def fake(sizes, n_d, rank, align, bucket):
+        lay = zero.zero_layout(sizes, n_d, rank, align)
+        S = lay.info["shard"]
+        pieces = [(0, S)] if bucket <= 0 else [(b, min(bucket, S - b)) for b in range(0, S, bucket)]
+        return types.SimpleNamespace(pieces=lambda: pieces, segments=lay.segments)
+
+    W = synth.WORKLOADS
+    for name, want in (("gpt-7.5b", True), ("gpt2-1.5b", True), ("llama-70b", True), ("llama-7b", False)):
+        wl = W[name]
+        assert bench.single_launch_calls(fake(wl.sizes, wl.n_d, wl.rank, wl.align, wl.bucket), True) == want, name
+    many = fake([10] * 100, 1, 0, 1, 0)
+    assert not bench.single_launch_calls(many, True) and bench.single_launch_calls(many, False)

@@ -38,6 +38,7 @@ def test_bench_json_line():
     fused = d["config"]["unpack"] == "fused into AdamW"
     assert fused                                   # the default path
     assert roof["algorithmic_bytes_per_launch"] == 28 * S + 2 * S    # the tiny shard has no padding
+    assert roof["timed_launches"] >= 1 and "note" not in roof        # one launch per update call
     parallel = len(os.sched_getaffinity(0)) > 1
     for base in ("cpu_baseline", "cpu_baseline_parallel") if parallel else ("cpu_baseline",):
         b = d[base]

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda")
-CUT = 1 << 27                       # a range longer than this takes several launches
+CUT = zero.ZERO_ADAMW_LAUNCH_ELEMS    # a range longer than this takes several launches
 
 
 def cuts(b, c):
@@ -29,7 +29,7 @@ def cuts(b, c):
     return [b + j * chunk for j in range(1, k) if b + j * chunk < b + c]
 
 
-def fused_cuts(lay, b, c, max_pieces=64):
+def fused_cuts(lay, b, c, max_pieces=zero.ZERO_PIECES_PER_LAUNCH):
     """Where the fused update cuts [b, b + c): the same launch length, and a
     launch in which more than 64 tensor pieces start ends at its 64th."""
     starts = sorted(max(g.dst_off, b) for g in lay.segments
