@@ -742,7 +742,9 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const Ad
   // (Issuing the lane's first loads before the clip coefficient, which every
   // wave forms in a chain of dependent loads and adds, measured 559-563 us at
   // the 7.5B shard against 559-560 us as written: that chain is not what
-  // limits the stream.)
+  // limits the stream. Loading eight ranks' sums per scalar load instead of
+  // one took the 24.3 M-element shard from 121 to 119.5 us but the 7.5B
+  // shard from 559 to 562 us.)
   const int64_t b_lo = (a.u_begin + int64_t(blockIdx.x) * kAdamThreads) << 2;
   const int hint = U.n > 0 && b_lo >= U.lo[0] && b_lo < U.lo[U.n] ? unpack_piece(U, b_lo) : -1;
   const float c = clip_coefficient(a);
