@@ -159,3 +159,42 @@ def test_cpu_adamw_random_cases(seed):
                              max_norm=float(rng.choice([0.0, 1.0, 1e-3])))
         _case(n, begin, count, int(rng.choice([1, 2, 10, 1000])), ohp, int(rng.integers(1, 200)),
               int(rng.integers(0, 9)), seed=int(rng.integers(0, 1 << 30)))
+
+
+def test_cpu_adamw_concurrent_callers():
+    """Several host threads calling the update at once (ctypes drops the
+    interpreter lock during the call): the library runs the calls one after
+    another on its pool, and every caller gets the bits of a lone call."""
+    import threading
+
+    rng = np.random.default_rng(77)
+    n = 200_003
+    cases = []
+    for k in range(4):
+        bits = synth.to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        state = to_tiles((rng.standard_normal(n) * 0.02).astype(np.float32),
+                         (rng.standard_normal(n) * 1e-4).astype(np.float32),
+                         np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32))
+        cases.append((bits, state, np.array([0.5 + k, 1.5])))
+    hp = _hp(O.AdamWHParams(), 7)
+
+    def run(k, reps, out):
+        bits, state0, parts = cases[k]
+        state, param = state0.copy(), np.zeros(n, np.uint16)
+        for _ in range(reps):
+            zero.zero_cpu_adamw_step(bits, state, param, n, 0, n, hp, parts, 2, 3)
+        out[k] = (state, param)
+
+    alone = {}
+    for k in range(4):
+        run(k, 3, alone)
+    together = {}
+    threads = [threading.Thread(target=run, args=(k, 3, together)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert len(together) == 4
+    for k in range(4):
+        assert np.array_equal(together[k][0].view(np.uint32), alone[k][0].view(np.uint32)), k
+        assert np.array_equal(together[k][1], alone[k][1]), k
