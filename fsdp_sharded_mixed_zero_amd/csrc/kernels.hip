@@ -578,15 +578,61 @@ __device__ __forceinline__ float grad_at(const AdamWArgs& a, int64_t e) {
   else return static_cast<const float*>(a.g)[e];
 }
 
+// ------------------------------------------------------------ stream loads
+// The vector path loads the gradient and the state with buffer instructions
+// carrying the sc1 and nt cache bits (device scope, non-temporal): data read
+// once goes to the L2 without passing through the CU's vector L1. Measured at
+// the 7.5B shard: the fused update 545 us against 555 us with non-temporal
+// global loads. The same bits on the stores made each step ~3 us slower at
+// the GPT-2 shard (the write-back at the end of the kernel), so the stores
+// stay non-temporal global stores. A buffer resource addresses 32-bit byte
+// offsets from its base: each launch gets resources based at its first tile,
+// and a launch spans at most kAdamLaunchElems elements (plus rounding to
+// whole tiles), whose state fits those offsets.
+
+constexpr int kStreamLoadAux = 16 | 2;        // sc1 | nt
+constexpr int kBufferWord3 = 0x00020000;      // raw (untyped) buffer access, gfx9 resource format
+static_assert(12 * (kAdamLaunchElems + 3 * kTile) < (int64_t(1) << 31), "a launch's state fits 32-bit offsets");
+
+template <typename G>
+struct StreamLoads {
+  __amdgpu_buffer_rsrc_t state, grad;
+  const float* sbase;   // the state of the launch's first tile
+  int64_t e0;           // that tile's first element
+};
+
+// The resources of a launch over [a.begin, a.end): the tiles it touches.
+template <typename G>
+__device__ __forceinline__ StreamLoads<G> stream_loads(const AdamWArgs& a) {
+  const int64_t t_lo = (a.begin >> kTileLog2) << kTileLog2;
+  const int64_t t_up = ((a.end + kTile - 1) >> kTileLog2) << kTileLog2;
+  const int64_t t_hi = t_up < a.n_state ? t_up : a.n_state;
+  StreamLoads<G> r;
+  r.e0 = t_lo;
+  r.sbase = a.state + 3 * t_lo;
+  r.state = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(r.sbase), 0, int(12 * (t_hi - t_lo)), kBufferWord3);
+  r.grad = __builtin_amdgcn_make_buffer_rsrc(const_cast<G*>(static_cast<const G*>(a.g) + t_lo), 0,
+                                             int(int64_t(sizeof(G)) * (t_hi - t_lo)), kBufferWord3);
+  return r;
+}
+
 // The 4 gradients of the unit at element e (a multiple of 4).
 template <typename G>
-__device__ __forceinline__ f32x4 grad4(const AdamWArgs& a, int64_t e) {
+__device__ __forceinline__ f32x4 grad4(const StreamLoads<G>& ld, int64_t e) {
+  const int off = int((e - ld.e0) * int64_t(sizeof(G)));
   if constexpr (sizeof(G) == 2) {
-    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.g) + e));
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(ld.grad, off, 0, kStreamLoadAux);
     return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
   } else {
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(a.g) + e));
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ld.grad, off, 0, kStreamLoadAux));
   }
+}
+
+// The 4 state values at s (a 16-byte aligned master, m or v slot of the launch).
+template <typename G>
+__device__ __forceinline__ f32x4 state4(const StreamLoads<G>& ld, const float* s) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ld.state, int((s - ld.sbase) * 4), 0,
+                                                                         kStreamLoadAux));
 }
 
 // One element; returns the bf16 parameter it stores.
@@ -607,6 +653,7 @@ __device__ __forceinline__ uint16_t adamw_scalar(const AdamWArgs& a, float c, in
 template <typename G>
 __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs a) {
   const float c = clip_coefficient(a);
+  const StreamLoads<G> ld = stream_loads<G>(a);
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
   for (int64_t u = a.u_begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < a.u_end; u += stride) {
     const int64_t e = u << 2;
@@ -619,10 +666,10 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_vec_kernel(const AdamWArgs
     f32x4* ps = reinterpret_cast<f32x4*>(s);
     f32x4* ms = reinterpret_cast<f32x4*>(s + L);
     f32x4* vs = reinterpret_cast<f32x4*>(s + 2 * L);
-    const f32x4 g4 = grad4<G>(a, e);
-    const f32x4 p4 = __builtin_nontemporal_load(ps);
-    const f32x4 m4 = __builtin_nontemporal_load(ms);
-    const f32x4 v4 = __builtin_nontemporal_load(vs);
+    const f32x4 g4 = grad4<G>(ld, e);
+    const f32x4 p4 = state4<G>(ld, s);
+    const f32x4 m4 = state4<G>(ld, s + L);
+    const f32x4 v4 = state4<G>(ld, s + 2 * L);
     float p[4] = {p4[0], p4[1], p4[2], p4[3]};
     float m[4] = {m4[0], m4[1], m4[2], m4[3]};
     float v[4] = {v4[0], v4[1], v4[2], v4[3]};
@@ -752,6 +799,7 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const Ad
   const int64_t b_lo = (a.u_begin + int64_t(blockIdx.x) * kAdamThreads) << 2;
   const int hint = U.n > 0 && b_lo >= U.lo[0] && b_lo < U.lo[U.n] ? unpack_piece(U, b_lo) : -1;
   const float c = clip_coefficient(a);
+  const StreamLoads<G> ld = stream_loads<G>(a);
   const int64_t stride = int64_t(gridDim.x) * kAdamThreads;
   for (int64_t u = a.u_begin + int64_t(blockIdx.x) * kAdamThreads + threadIdx.x; u < a.u_end; u += stride) {
     const int64_t e = u << 2;
@@ -764,10 +812,10 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_unpack_vec_kernel(const Ad
     f32x4* ps = reinterpret_cast<f32x4*>(s);
     f32x4* ms = reinterpret_cast<f32x4*>(s + L);
     f32x4* vs = reinterpret_cast<f32x4*>(s + 2 * L);
-    const f32x4 g4 = grad4<G>(a, e);
-    const f32x4 p4 = __builtin_nontemporal_load(ps);
-    const f32x4 m4 = __builtin_nontemporal_load(ms);
-    const f32x4 v4 = __builtin_nontemporal_load(vs);
+    const f32x4 g4 = grad4<G>(ld, e);
+    const f32x4 p4 = state4<G>(ld, s);
+    const f32x4 m4 = state4<G>(ld, s + L);
+    const f32x4 v4 = state4<G>(ld, s + 2 * L);
     float p[4] = {p4[0], p4[1], p4[2], p4[3]};
     float m[4] = {m4[0], m4[1], m4[2], m4[3]};
     float v[4] = {v4[0], v4[1], v4[2], v4[3]};
