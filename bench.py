@@ -129,10 +129,37 @@ def steps_traced(counts, wl, S):
     return counts["sqnorm_final_kernel"] / pieces
 
 
+def code_text(text):
+    """C++ source with its comments removed and blank space collapsed (string
+    and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
+    """sha256 of the kernels' code (comments and blank space aside): the
+    counters of a profile stay valid across comment edits, not code edits."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()
 
 
 def traffic_file(workload):
@@ -193,7 +220,7 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
                 f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline",
                 f"python bench.py --workload {wl.name} {mode} --pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
-            "kernel_source_sha256": source_hash(),
+            "kernel_code_sha256": source_hash(),
             "calibration": {"kernel": copy, "source": source, "known_read_kib": known_kib,
                             "known_write_kib": known_kib, "fetch_factor": round(f_fetch, 5),
                             "write_factor": round(f_write, 5)},
@@ -221,7 +248,7 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
              f"--no-cpu-baseline --no-copy-ceiling",
              f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
              f"--stats-summary {stats_dir}", "",
-             f"kernels.hip sha256: `{source_hash()}`", "",
+             f"kernels.hip code sha256 (comments and blank space aside): `{source_hash()}`", "",
              f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "
              f"kernel divided by its launches per step.", "",
              "| kernel | calls | launches/step | avg us | min us | max us | algorithmic bytes/launch | "
@@ -263,7 +290,7 @@ def measured_traffic(workload, kernel):
     if not os.path.exists(path):
         return None
     data = _json.load(open(path))
-    if data.get("kernel_source_sha256") != source_hash():
+    if data.get("kernel_code_sha256") != source_hash():
         return None
     return data["kernels"].get(kernel, {}).get("traffic_bytes")
 

@@ -8,7 +8,8 @@
 // so the waves in flight at any moment touch a compact window of each stream.
 // Persistent grid-stride loops and lanes that own 32 contiguous bytes (two
 // half-filled instructions per stream) both measured 10-20% slower. Loads and
-// stores are non-temporal: nothing is reused within a step.
+// stores are non-temporal: nothing is reused within a step (the update's
+// loads also carry device scope, see "stream loads").
 //
 //   copy_pieces_kernel<SQ>    pack (tensors -> shard) and unpack (shard ->
 //                             tensors); with SQ the pack also sums squares

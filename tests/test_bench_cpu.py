@@ -196,3 +196,13 @@ def test_single_launch_calls():
         assert bench.single_launch_calls(fake(wl.sizes, wl.n_d, wl.rank, wl.align, wl.bucket), True) == want, name
     many = fake([10] * 100, 1, 0, 1, 0)
     assert not bench.single_launch_calls(many, True) and bench.single_launch_calls(many, False)
+
+
+def test_code_hash_ignores_comments_not_code():
+    src = 'int f(int x) { // a comment\n  return x + 1; /* block\n comment */ }\nconst char* s = "a // b /* c";\n'
+    same = 'int f(int x) {\n  return x + 1;   }\n// other words\nconst char* s = "a // b /* c";'
+    other = 'int f(int x) { return x + 2; }\nconst char* s = "a // b /* c";'
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(other)
+    assert '"a // b /* c"' in bench.code_text(src)
+    assert len(bench.source_hash()) == 64
