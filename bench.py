@@ -371,6 +371,7 @@ def cpu_baseline(wl, seconds):
             done += sample[1]
             runs += 1
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": (f"{runs} runs over {len(samples)} distinct chunks of {ORACLE_CHUNK} elements of the "
                        f"{wl.name} rank-{wl.rank} shard ({done} elements, {spent:.1f} s of oracle time), "
                        f"numpy float64 oracle on one host thread")}
@@ -415,6 +416,7 @@ def cpu_baseline_parallel(wl, seconds, workers):
         pr.join()
     rate = sum(d / s for d, s in out)
     return {"value": rate, "unit": "params/s", "cores": workers, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": (f"{workers} processes, one host thread each, each on its own chunk of {ORACLE_CHUNK} "
                        f"elements of the {wl.name} rank-{wl.rank} shard for about {seconds:.0f} s "
                        f"({sum(d for d, _ in out)} elements in all)")}

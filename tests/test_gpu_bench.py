@@ -43,6 +43,7 @@ def test_bench_json_line():
     for base in ("cpu_baseline", "cpu_baseline_parallel") if parallel else ("cpu_baseline",):
         b = d[base]
         assert b["kind"] == "oracle" and b["unit"] == "params/s" and b["value"] > 0 and b["cores"] >= 1
+        assert b["host_cpus"] >= b["affinity_cpus"] >= b["cores"]
         assert b["sample"]
     assert d["cpu_baseline"]["cores"] == 1
     assert d["copy_ceiling"]["copied_correctly"] is True and d["copy_ceiling"]["GBps"] > 0
