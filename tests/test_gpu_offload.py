@@ -1,4 +1,4 @@
-"""ZeRO-Offload on the GPU machine: the offloaded step (GPU pack + norm, PCIe
+"""ZeRO-Offload on the GPU: the offloaded step (GPU pack + norm, PCIe
 copies through pinned staging slots, AdamW on the host cores, GPU unpack)
 against the oracle, and against the all-GPU step with the same inputs and
 buckets, which it must equal bit for bit (same fp32 operation sequence)."""
