@@ -9,11 +9,10 @@ Sources (pages, not code):
   * "第 5 课：ZeRO 与 FSDP", section 2: each rank keeps a 1/N_d slice.
 
 Readings where the pages are silent: tensors are concatenated in list order
-with no gaps between them; the
-flat buffer is padded at the tail only, up to P = ceil(Psi / (N_d*A)) * N_d*A
-elements, so every rank owns S = P / N_d elements and every shard starts on a
-multiple of A elements; zero-size tensors own no elements and produce no
-segment.
+with no gaps between them; the flat buffer is padded at the tail only, up to
+P = ceil(Psi / (N_d*A)) * N_d*A elements, so every rank owns S = P / N_d
+elements and every shard starts on a multiple of A elements; zero-size
+tensors own no elements and produce no segment.
 """
 
 from __future__ import annotations
