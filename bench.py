@@ -554,9 +554,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one rank's shard on one GPU; runs on more than one GPU are "
-              "not part of this build (the collectives around the step are not implemented)",
-              file=sys.stderr)
+        print("bench.py measures one rank's shard on one GPU; it does not run on more than one GPU "
+              "(the collectives around the step are not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
