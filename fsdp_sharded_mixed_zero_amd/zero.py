@@ -138,6 +138,8 @@ def _ptr(x):
     if not getattr(x, "is_cuda", False):
         raise TypeError(f"device memory expected, got {type(x).__name__}"
                         f"{' on ' + str(x.device) if hasattr(x, 'device') else ''}")
+    if not x.is_contiguous():
+        raise ValueError("a contiguous tensor is expected: the library reads consecutive elements")
     return x.data_ptr()
 
 
@@ -308,9 +310,13 @@ def _host_ptr(x):
     if x is None or isinstance(x, int):
         return x
     if hasattr(x, "ctypes"):
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("a contiguous array is expected: the library reads consecutive elements")
         return x.ctypes.data
     if getattr(x, "is_cuda", False):
         raise TypeError("host memory expected, got a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("a contiguous tensor is expected: the library reads consecutive elements")
     return x.data_ptr()
 
 

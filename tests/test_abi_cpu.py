@@ -235,6 +235,17 @@ def test_binding_refuses_short_pointer_arrays():
             call()
 
 
+def test_binding_refuses_strided_host_buffers():
+    """The host update reads consecutive elements: a strided numpy array or
+    CPU tensor is refused before the call."""
+    torch = pytest.importorskip("torch")
+    hp = zero.hparams(step=1)
+    state = np.zeros(3 * 8, np.float32)
+    for bad in (np.zeros(16, np.uint16)[::2], torch.zeros(16, dtype=torch.int16)[::2]):
+        with pytest.raises(ValueError):
+            zero.zero_cpu_adamw_step(bad, state, np.zeros(8, np.uint16), 8, 0, 8, hp, np.ones(1), 1)
+
+
 def test_binding_refuses_memory_on_the_wrong_side():
     """Host buffers given to a device entry point (and device buffers given to
     the host update) are refused by the binding before anything runs."""

@@ -268,6 +268,20 @@ def test_pack_unpack_many_pieces_per_slot(sizes):
             assert np.array_equal(to_host_u16(o), r)
 
 
+def test_binding_refuses_strided_device_tensors():
+    """The kernels read consecutive elements: a strided view is refused by the
+    binding before anything is launched."""
+    g = to_dev_u16(np.zeros(64, np.uint16))
+    st = torch.zeros(3 * 32, dtype=torch.float32, device=DEV)
+    p = sentinel(32)
+    with pytest.raises(ValueError):
+        zero.zero_adamw_step(g[::2], st, p, 32, 0, 32, zero.hparams(max_norm=0.0, step=1), None, 0)
+    h = zero.zero_layout([32], 1, 0, 1)
+    with pytest.raises(ValueError):
+        zero.zero_pack_grads(h, [g[::2]], p, 0, 32)
+    assert (to_host_u16(p) == synth.SENTINEL).all()
+
+
 def test_pack_rejects_missing_tensor_pointer():
     sizes = [100, 100]
     h = zero.zero_layout(sizes, 1, 0, 1)
