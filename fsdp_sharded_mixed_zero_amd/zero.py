@@ -169,18 +169,43 @@ def _tensor_array(layout, items):
     """The per-tensor pointer array of a call on `layout`. The library reads
     one pointer per tensor of the layout, so a shorter array is refused here
     (it would be read past its end)."""
+    if not isinstance(items, ctypes.Array):
+        for i, t in enumerate(items):
+            if i < len(layout.sizes):
+                _need(t, 2 * layout.sizes[i], f"tensor {i}")
     arr = _ptr_array(items)
     if len(arr) < layout.n_tensors:
         raise ValueError(f"{len(arr)} tensor pointers for a layout of {layout.n_tensors} tensors")
     return arr
 
 
-class Layout:
-    """Owner of a zero_layout_t handle."""
+def _need(x, nbytes: int, what: str):
+    """Refuse a tensor or array smaller than the bytes the call reaches in it
+    (a kernel would read or write past its end). Raw addresses are the
+    caller's to size."""
+    if x is None or isinstance(x, int) or not hasattr(x, "nbytes"):
+        return
+    if int(x.nbytes) < nbytes:
+        raise ValueError(f"{what}: {int(x.nbytes)} bytes given, the call reaches {nbytes}")
 
-    def __init__(self, handle: int, n_tensors: int):
+
+def _need_update(grad, gsize, state, param, n_state, begin, count, rank_sqnorms, n_ranks):
+    if count <= 0:
+        return
+    _need(grad, gsize * (begin + count), "gradient")
+    _need(state, 12 * n_state, "state")
+    _need(param, 2 * (begin + count), "parameter shard")
+    if n_ranks > 0:
+        _need(rank_sqnorms, 8 * n_ranks, "rank sums of squares")
+
+
+class Layout:
+    """Owner of a zero_layout_t handle (and of the size list it was made from)."""
+
+    def __init__(self, handle: int, n_tensors: int, sizes=()):
         self.handle = handle
         self.n_tensors = n_tensors
+        self.sizes = tuple(sizes)
 
     def close(self):
         if self.handle:
@@ -207,7 +232,7 @@ def zero_layout(sizes, n_d: int, rank: int, align_elems: int = 128) -> Layout:
     arr = (_I64 * max(1, len(sizes)))(*sizes)
     h = _VP()
     _check("zero_layout", library().zero_layout(arr, len(sizes), n_d, rank, align_elems, ctypes.byref(h)))
-    return Layout(h.value, len(sizes))
+    return Layout(h.value, len(sizes), sizes)
 
 
 def zero_layout_free(layout: Layout) -> None:
@@ -231,6 +256,8 @@ def zero_layout_segments(layout: Layout):
 
 def zero_pack_grads(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, stream=None):
     arr = _tensor_array(layout, tensor_grads)
+    if count > 0:
+        _need(grad_shard, 2 * (begin + count), "gradient shard")
     _check("zero_pack_grads", library().zero_pack_grads(
         layout.handle, arr, _ptr(grad_shard), begin, count, _stream(stream)))
 
@@ -242,6 +269,9 @@ def zero_pack_sqnorm_workspace_bytes(layout: Layout, begin: int, count: int) -> 
 def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, out,
                            accumulate: bool, workspace, ws_bytes: int | None = None, stream=None):
     arr = _tensor_array(layout, tensor_grads)
+    if count > 0:
+        _need(grad_shard, 2 * (begin + count), "gradient shard")
+    _need(out, 8, "output")
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_pack_grads_sqnorm", library().zero_pack_grads_sqnorm(
@@ -251,6 +281,8 @@ def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int,
 
 def zero_unpack_params(layout: Layout, param_shard, tensor_params, begin: int, count: int, stream=None):
     arr = _tensor_array(layout, tensor_params)
+    if count > 0:
+        _need(param_shard, 2 * (begin + count), "parameter shard")
     _check("zero_unpack_params", library().zero_unpack_params(
         layout.handle, _ptr(param_shard), arr, begin, count, _stream(stream)))
 
@@ -261,6 +293,9 @@ def zero_sqnorm_workspace_bytes(count: int) -> int:
 
 def zero_shard_sqnorm(grad, count: int, out, accumulate: bool, workspace, ws_bytes: int | None = None,
                       stream=None):
+    if count > 0:
+        _need(grad, 2 * count, "gradient")
+    _need(out, 8, "output")
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_shard_sqnorm", library().zero_shard_sqnorm(
@@ -275,6 +310,7 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_no
 
 def zero_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
                     rank_sqnorms, n_ranks: int, stream=None):
+    _need_update(grad, 2, state, param, n_state, begin, count, rank_sqnorms, n_ranks)
     _check("zero_adamw_step", library().zero_adamw_step(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
@@ -282,6 +318,7 @@ def zero_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp
 
 def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count: int,
                             hp: zero_adamw_hparams, rank_sqnorms, n_ranks: int, stream=None):
+    _need_update(grad, 4, state, param, n_state, begin, count, rank_sqnorms, n_ranks)
     _check("zero_adamw_step_f32grad", library().zero_adamw_step_f32grad(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
@@ -290,6 +327,7 @@ def zero_adamw_step_f32grad(grad, state, param, n_state: int, begin: int, count:
 def zero_adamw_step_unpack(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
                            rank_sqnorms, n_ranks: int, layout: Layout, tensor_params, stream=None):
     arr = _tensor_array(layout, tensor_params)
+    _need_update(grad, 2, state, param, n_state, begin, count, rank_sqnorms, n_ranks)
     _check("zero_adamw_step_unpack", library().zero_adamw_step_unpack(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))
@@ -299,6 +337,7 @@ def zero_adamw_step_f32grad_unpack(grad, state, param, n_state: int, begin: int,
                                    hp: zero_adamw_hparams, rank_sqnorms, n_ranks: int, layout: Layout,
                                    tensor_params, stream=None):
     arr = _tensor_array(layout, tensor_params)
+    _need_update(grad, 4, state, param, n_state, begin, count, rank_sqnorms, n_ranks)
     _check("zero_adamw_step_f32grad_unpack", library().zero_adamw_step_f32grad_unpack(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, layout.handle, arr, _stream(stream)))
@@ -322,19 +361,32 @@ def _host_ptr(x):
 
 def zero_cpu_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp: zero_adamw_hparams,
                         rank_sqnorms, n_ranks: int, n_threads: int = 0):
-    """Host memory throughout (numpy arrays or CPU tensors)."""
+    """Host memory throughout (numpy arrays or CPU tensors). The gradient and
+    parameter buffers hold the range only (element begin first)."""
+    if count > 0:
+        _need(grad, 2 * count, "gradient")
+        _need(state, 12 * n_state, "state")
+        _need(param, 2 * count, "parameters")
+        if n_ranks > 0:
+            _need(rank_sqnorms, 8 * n_ranks, "rank sums of squares")
     _check("zero_cpu_adamw_step", library().zero_cpu_adamw_step(
         _host_ptr(grad), _host_ptr(state), _host_ptr(param), n_state, begin, count, ctypes.byref(hp),
         _host_ptr(rank_sqnorms), n_ranks, n_threads))
 
 
 def zero_accumulate_grads(grad, acc, count: int, first: bool, stream=None):
+    if count > 0:
+        _need(grad, 2 * count, "gradient")
+        _need(acc, 4 * count, "accumulator")
     _check("zero_accumulate_grads", library().zero_accumulate_grads(
         _ptr(grad), _ptr(acc), count, 1 if first else 0, _stream(stream)))
 
 
 def zero_shard_sqnorm_f32(grad, count: int, out, accumulate: bool, workspace, ws_bytes: int | None = None,
                           stream=None):
+    if count > 0:
+        _need(grad, 4 * count, "gradient")
+    _need(out, 8, "output")
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("zero_shard_sqnorm_f32", library().zero_shard_sqnorm_f32(
@@ -343,10 +395,16 @@ def zero_shard_sqnorm_f32(grad, count: int, out, accumulate: bool, workspace, ws
 
 
 def zero_state_import(master, m, v, state, n: int, stream=None):
+    for x, what in ((master, "master"), (m, "m"), (v, "v")):
+        _need(x, 4 * n, what)
+    _need(state, 12 * n, "state")
     _check("zero_state_import", library().zero_state_import(
         _ptr(master), _ptr(m), _ptr(v), _ptr(state), n, _stream(stream)))
 
 
 def zero_state_export(state, master, m, v, n: int, stream=None):
+    for x, what in ((master, "master"), (m, "m"), (v, "v")):
+        _need(x, 4 * n, what)
+    _need(state, 12 * n, "state")
     _check("zero_state_export", library().zero_state_export(
         _ptr(state), _ptr(master), _ptr(m), _ptr(v), n, _stream(stream)))

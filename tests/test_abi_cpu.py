@@ -252,7 +252,7 @@ def test_binding_refuses_memory_on_the_wrong_side():
     torch = pytest.importorskip("torch")
     import numpy as np
 
-    x = torch.zeros(8, dtype=torch.float32)
+    x = torch.zeros(24, dtype=torch.float32)        # large enough for every buffer below
     hp = zero.hparams(step=1)
     with pytest.raises(TypeError):
         zero.zero_adamw_step(x, x, x, 8, 0, 8, hp, None, 0)
@@ -260,3 +260,31 @@ def test_binding_refuses_memory_on_the_wrong_side():
         zero.zero_accumulate_grads(np.zeros(8, np.uint16), x, 8, True)
     with pytest.raises(TypeError):
         zero.zero_state_import(x, x, x, x, 8)
+
+
+def test_binding_refuses_short_buffers():
+    """A tensor or array smaller than the bytes a call reaches in it is
+    refused before the call (a kernel would run past its end)."""
+    torch = pytest.importorskip("torch")
+    hp = zero.hparams(step=1, max_norm=0.0)
+    n = 100
+    with pytest.raises(ValueError, match="state"):
+        zero.zero_cpu_adamw_step(np.zeros(n, np.uint16), np.zeros(3 * n - 1, np.float32), np.zeros(n, np.uint16),
+                                 n, 0, n, hp, None, 0)
+    with pytest.raises(ValueError, match="parameters"):
+        zero.zero_cpu_adamw_step(np.zeros(n, np.uint16), np.zeros(3 * n, np.float32), np.zeros(n - 1, np.uint16),
+                                 n, 0, n, hp, None, 0)
+    with pytest.raises(ValueError, match="rank sums"):
+        zero.zero_cpu_adamw_step(np.zeros(n, np.uint16), np.zeros(3 * n, np.float32), np.zeros(n, np.uint16),
+                                 n, 0, n, zero.hparams(step=1), np.ones(3), 4)
+    # a bf16 tensor where the fp32 state belongs: half the bytes
+    with pytest.raises(ValueError, match="state"):
+        zero.zero_cpu_adamw_step(np.zeros(n, np.uint16), torch.zeros(3 * n, dtype=torch.bfloat16),
+                                 np.zeros(n, np.uint16), n, 0, n, hp, None, 0)
+    lay = zero.zero_layout([100, 28], 1, 0, 1)
+    with pytest.raises(ValueError, match="tensor 1"):
+        zero.zero_pack_grads(lay, [torch.zeros(100, dtype=torch.int16), torch.zeros(27, dtype=torch.int16)], 0, 0,
+                             8)
+    # an empty range reaches nothing
+    zero.zero_cpu_adamw_step(np.zeros(0, np.uint16), np.zeros(0, np.float32), np.zeros(0, np.uint16), n, 5, 0,
+                             hp, None, 0)

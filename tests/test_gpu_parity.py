@@ -291,7 +291,9 @@ def test_pack_rejects_missing_tensor_pointer():
     # a range that does not touch the missing tensor is fine
     zero.zero_pack_grads(h, [to_dev_u16(np.ones(100, np.uint16)), None], shard, 0, 100)
     assert (to_host_u16(shard)[:100] == 1).all()
-    with pytest.raises(zero.ZeroError):
+    with pytest.raises(zero.ZeroError):        # the library's range check (raw address: not sized here)
+        zero.zero_pack_grads(h, [None, None], shard.data_ptr(), 150, 60)
+    with pytest.raises(ValueError):            # the binding refuses the tensor, past whose end it would write
         zero.zero_pack_grads(h, [None, None], shard, 150, 60)
 
 
@@ -436,8 +438,12 @@ def test_adamw_padding_and_empty():
     assert (to_host_u16(o) == 0).all()
     # count == 0 touches nothing, even with NULL buffers
     zero.zero_adamw_step(None, None, None, 0, 0, 0, zero.hparams(step=5), parts, 1)
-    with pytest.raises(zero.ZeroError):
+    with pytest.raises(zero.ZeroError):        # the library's range check (raw addresses: not sized here)
+        zero.zero_adamw_step(g.data_ptr(), s.data_ptr(), o.data_ptr(), n, 990, 11, zero.hparams(step=5), parts, 1)
+    with pytest.raises(ValueError):            # the binding refuses tensors the range would run past
         zero.zero_adamw_step(g, s, o, n, 990, 11, zero.hparams(step=5), parts, 1)
+    with pytest.raises(ValueError):            # a bf16 state: half the bytes of the fp32 one
+        zero.zero_adamw_step(g, s.view(torch.int16)[:3 * n], o, n, 0, n, zero.hparams(step=5), parts, 1)
 
 
 def test_adamw_nan_norm_poisons_update():

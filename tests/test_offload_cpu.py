@@ -82,7 +82,7 @@ def test_cpu_adamw_threads_agree():
 
 def test_cpu_adamw_rejects_bad_arguments():
     hp = zero.hparams(step=1)
-    x = np.zeros(8, np.float32)
+    x = np.zeros(3 * 8, np.float32)          # the state of 8 elements (the library's checks are tested)
     with pytest.raises(zero.ZeroError):
         zero.zero_cpu_adamw_step(np.zeros(8, np.uint16), x, np.zeros(8, np.uint16), 8, 4, 5, hp,
                                  np.ones(1), 1)
