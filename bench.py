@@ -121,12 +121,13 @@ def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unp
     return S, real, out
 
 
-def steps_traced(counts, wl, S):
+def steps_traced(counts, wl, S, combine=False):
     """Steps a trace covers (warm-up included): the sum-of-squares final
-    kernel runs once per bucket in every mode, whereas an update over more
-    than 64 tensor pieces takes several launches."""
+    kernel runs once per bucket in every mode (plus once for the combine of a
+    bucketed default step), whereas an update over more than 64 tensor pieces
+    takes several launches."""
     pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
-    return counts["sqnorm_final_kernel"] / pieces
+    return counts["sqnorm_final_kernel"] / (pieces + (1 if combine and pieces > 1 else 0))
 
 
 def code_text(text):
@@ -189,7 +190,7 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
     write, n_w = load(write_dir, "WRITE_SIZE")
     mode = f"--steps {steps} --warmup {warmup}" + (" --separate-unpack --no-copy-ceiling" if separate_unpack else "")
     S, real, algo = algorithmic_bytes(wl, separate_unpack=separate_unpack)
-    steps = steps_traced(n_f, wl, S)
+    steps = steps_traced(n_f, wl, S, combine=True)
     update = update_kernel(separate_unpack=separate_unpack)
     per_dispatch = {k: algo[k] / (n_f[k] / steps) for k in algo if k in n_f}
     copy = "copy_pieces_kernel<false>"
@@ -237,7 +238,27 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat, separate_unpack)
     rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
-    steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S)
+    # busy time of each kernel: the union of its launches' intervals (launches
+    # on two streams overlap, and each one's duration then includes time the
+    # other stream shares)
+    spans = {}
+    for tpath in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(tpath)):
+            spans.setdefault(kernel_name(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    busy_ns = {}
+    for k, iv in spans.items():
+        total, end = 0, None
+        for a, b in sorted(iv):
+            if end is None or a > end:
+                total += b - a
+                end = b
+            elif b > end:
+                total += b - end
+                end = b
+        busy_ns[k] = total
+    steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S,
+                             combine=accum == 1 and not separate_norm and not flat)
     mode = ((f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "") +
             (" --flat" if flat else "") + (" --separate-unpack" if separate_unpack else ""))
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
@@ -251,9 +272,11 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
              f"kernels.hip code sha256 (comments and blank space aside): `{source_hash()}`", "",
              f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "
              f"kernel divided by its launches per step.", "",
+             "Busy us/step is the union of the kernel's launch intervals per step (the same as launches x avg "
+             "when launches do not overlap); GB/s (busy) divides the step's bytes for the kernel by it.", "",
              "| kernel | calls | launches/step | avg us | min us | max us | algorithmic bytes/launch | "
-             "GB/s at avg | % of 8 TB/s |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             "GB/s at avg | % of 8 TB/s | busy us/step | GB/s (busy) | % (busy) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for short, row in rows.items():
         if short not in algo and not short.startswith("sqnorm_final"):
             continue
@@ -263,8 +286,13 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
         b = algo[short] / per_step if short in algo else None
         gbps = f"{b / (avg * 1e-6) / 1e9:.1f}" if b else "-"
         pct = f"{100 * b / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}" if b else "-"
+        busy = busy_ns.get(short, 0) / 1e3 / steps_run if busy_ns else None
+        step_b = algo.get(short)
+        bgbps = f"{step_b / (busy * 1e-6) / 1e9:.1f}" if busy and step_b else "-"
+        bpct = f"{100 * step_b / (busy * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}" if busy and step_b else "-"
         lines.append(f"| {short} | {calls} | {per_step:.2f} | {avg:.1f} | {float(row['MinNs']) / 1e3:.1f} | "
-                     f"{float(row['MaxNs']) / 1e3:.1f} | {int(b) if b else '-'} | {gbps} | {pct} |")
+                     f"{float(row['MaxNs']) / 1e3:.1f} | {int(b) if b else '-'} | {gbps} | {pct} | "
+                     f"{f'{busy:.1f}' if busy else '-'} | {bgbps} | {bpct} |")
     return "\n".join(lines) + "\n"
 
 
@@ -632,6 +660,7 @@ def main():
     call_bytes = algo["adamw"] / calls
     achieved = call_bytes / (call_ms * 1e-3) / 1e9
     single = single_launch_calls(rs, rs.fused_unpack)
+    bucketed, n_streams = rs.bucketed, rs.n_streams
     step_bytes = sum(algo.values())
     default_kernel = rs.bucket <= 0 and args.accum == 1 and not args.flat
     traffic = (measured_traffic(wl.name, update_kernel(args.accum, args.separate_unpack, args.flat))
@@ -657,7 +686,7 @@ def main():
                                else "pack + sum of squares -> clip+AdamW+bf16 cast with the unpack fused"),
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
                    "segments_in_shard": len(rs.segments), "adamw_step": wl.step,
-                   "bucket": rs.bucket,
+                   "bucket": rs.bucket, "streams": rs.n_streams,
                    "norm": "separate" if args.separate_norm or args.flat else "fused into pack",
                    "unpack": ("none (flat buffers)" if args.flat else
                               "separate" if args.separate_unpack else "fused into AdamW"),
@@ -670,11 +699,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
-    unit, units = ("launch", "launches") if single else ("call", "calls")
+    unit, units = ("phase", "phases") if bucketed else ("launch", "launches") if single else ("call", "calls")
     out["roofline"].update({
         f"algorithmic_bytes_per_{unit}": int(call_bytes), f"timed_{units}": len(timing["adamw"]),
         "events": f"around the AdamW {units} of every {EVENT_EVERY}th step of the timed region"})
-    if not single:
+    if bucketed:
+        out["roofline"]["note"] = (f"the update phase: one launch per bucket, the buckets dealt out to {n_streams} "
+                                   f"streams; achieved is the phase's bytes over its time")
+    elif not single:
         out["roofline"]["note"] = ("each update call runs as several kernel launches back to back (a range longer "
                                    "than ZERO_ADAMW_LAUNCH_ELEMS elements or touching more than "
                                    "ZERO_PIECES_PER_LAUNCH tensor pieces): achieved is per call")

@@ -1028,6 +1028,20 @@ extern "C" int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* 
   return zero::ok();
 }
 
+extern "C" int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_t accumulate,
+                                 hipStream_t stream) {
+  static const char* who = "zero_sum_partials";
+  if (n < 0) return fail(ZERO_EINVAL, "%s: n < 0", who);
+  if (d_out == nullptr) return fail(ZERO_EINVAL, "%s: NULL output", who);
+  if (n > 0 && d_partials == nullptr) return fail(ZERO_EINVAL, "%s: NULL partial sums", who);
+  if ((uintptr_t(d_partials) | uintptr_t(d_out)) & 7u) return fail(ZERO_EINVAL, "%s: misaligned pointer", who);
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, d_partials, n, d_out,
+                     accumulate ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
 // Checks the arguments of an update over [begin, begin+count) and fills the
 // kernel arguments (range fields for the whole range). *vec: the pointers
 // allow the vector path. With count == 0 it returns OK after the checks

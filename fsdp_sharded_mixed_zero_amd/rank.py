@@ -41,7 +41,7 @@ from . import synth, zero
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
                  fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
-                 accum_steps: int = 1, flat: bool = False, fused_unpack: bool = True):
+                 accum_steps: int = 1, flat: bool = False, fused_unpack: bool = True, streams: int = 2):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -92,6 +92,15 @@ class RankShard:
         ws = max(max(zero.zero_sqnorm_workspace_bytes(n),
                      zero.zero_pack_sqnorm_workspace_bytes(self.layout, b, n)) for b, n in self.pieces())
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=dev)
+        # buckets of the default step: each bucket's sum of squares in its own
+        # slot, combined once (zero_sum_partials), and the buckets dealt out
+        # to `streams` streams in turn
+        n_pieces = len(self.pieces())
+        self.bucketed = n_pieces > 1 and not flat and accum_steps == 1 and fused_norm
+        self.bucket_sq = torch.zeros(n_pieces, dtype=torch.float64, device=dev) if n_pieces > 1 else None
+        self.n_streams = max(1, int(streams)) if self.bucketed else 1
+        self.workspaces = [self.workspace] + [torch.empty_like(self.workspace) for _ in range(self.n_streams - 1)]
+        self.streams = [torch.cuda.Stream(device=dev) for _ in range(self.n_streams)] if self.n_streams > 1 else []
         if fill:
             self.fill_state()
             self.fill_grads(wl.step)
@@ -159,11 +168,17 @@ class RankShard:
         CUDA events recorded around its launches on the current stream, taken
         from the iterator ``events`` (pre-created, so timing adds no event
         creation to the step); ``phases`` limits the timed phases (each event
-        record costs GPU time between launches). ``before_micro(mb)`` runs
-        before each micro-batch when accumulating (to refill the gradients)."""
+        record costs GPU time between launches). A bucketed default step times
+        each phase as a whole (its buckets overlap on several streams).
+        ``before_micro(mb)`` runs before each micro-batch when accumulating (to
+        refill the gradients)."""
         hp = self.hparams(step)
         own = self.rank_sq[self.rank:self.rank + 1]
         pieces = self.pieces()
+        if self.bucketed:
+            self._step_buckets(hp, own, pieces, torch.cuda.current_stream() if stream is None else stream,
+                               timing, events, phases)
+            return
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
 
@@ -205,6 +220,62 @@ class RankShard:
                 self.wl.n_d, stream))
             mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
+
+    def pack_norm_buckets(self, own, stream, pieces=None):
+        """Pack + sum of squares of every bucket, each bucket's sum in its own
+        slot, on the step's streams in turn; then, on ``stream`` once all are
+        done, ``own`` = the slots added in a fixed order. The result does not
+        depend on the number of streams."""
+        pieces = self.pieces() if pieces is None else pieces
+        main = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+        for st in self.streams:
+            st.wait_stream(main)
+        for k, (b, n) in enumerate(pieces):
+            i = k % self.n_streams
+            st = self.streams[i].cuda_stream if self.streams else main.cuda_stream
+            zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, b, n, self.bucket_sq[k:k + 1],
+                                        False, self.workspaces[i], stream=st)
+        for st in self.streams:
+            main.wait_stream(st)
+        zero.zero_sum_partials(self.bucket_sq, len(pieces), own, False, stream=main.cuda_stream)
+
+    def _step_buckets(self, hp, own, pieces, stream, timing, events, phases):
+        """The default step over buckets: the packs on the streams in turn and
+        the combine, then the updates with the unpack fused on the streams in
+        turn (or the updates, then the unpacks). With timing, one event pair
+        spans each phase on the calling stream (the buckets of a phase overlap
+        on the streams)."""
+        main = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+
+        def timed(phase, fn):
+            if timing is None or (phases is not None and phase not in phases):
+                fn()
+                return
+            e0 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
+            e1 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            fn()
+            e1.record(main)
+            timing.setdefault(phase, []).append((e0, e1))
+
+        def on_streams(call):
+            for st in self.streams:
+                st.wait_stream(main)
+            for k, (b, n) in enumerate(pieces):
+                call(b, n, self.streams[k % self.n_streams].cuda_stream if self.streams else main.cuda_stream)
+            for st in self.streams:
+                main.wait_stream(st)
+
+        timed("pack_sqnorm", lambda: self.pack_norm_buckets(own, main, pieces))
+        if self.fused_unpack:
+            timed("adamw", lambda: on_streams(lambda b, n, st: zero.zero_adamw_step_unpack(
+                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq, self.wl.n_d,
+                self.layout, self.param_ptrs, st)))
+        else:
+            timed("adamw", lambda: on_streams(lambda b, n, st: zero.zero_adamw_step(
+                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq, self.wl.n_d, st)))
+            timed("unpack", lambda: on_streams(lambda b, n, st: zero.zero_unpack_params(
+                self.layout, self.param_shard, self.param_ptrs, b, n, st)))
 
     def _step_flat(self, hp, own, pieces, stream, mark):
         for k, (b, n) in enumerate(pieces):
@@ -349,8 +420,10 @@ class OffloadRank(RankShard):
         cs = torch.cuda.current_stream()
         stream = cs.cuda_stream
         own = self.rank_sq[self.rank:self.rank + 1]
-        for k, (b, n) in enumerate(self.pieces()):
-            zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, b, n, own, k > 0,
+        if self.bucketed:          # the same buckets and combine as the all-GPU step
+            self.pack_norm_buckets(own, cs)
+        else:
+            zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, 0, self.shard, own, False,
                                         self.workspace, stream=stream)
         self.packed.record(cs)
         self.d2h.wait_event(self.packed)

@@ -78,6 +78,7 @@ _SIGNATURES = {
     "zero_pack_grads_sqnorm": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP, _I32, _VP,
                                               ctypes.c_size_t, _VP]),
     "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
+    "zero_sum_partials": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
     "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                        ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
     "zero_adamw_step_f32grad": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
@@ -301,6 +302,14 @@ def zero_shard_sqnorm(grad, count: int, out, accumulate: bool, workspace, ws_byt
     _check("zero_shard_sqnorm", library().zero_shard_sqnorm(
         _ptr(grad), count, _ptr(out), 1 if accumulate else 0, _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def zero_sum_partials(partials, n: int, out, accumulate: bool = False, stream=None):
+    if n > 0:
+        _need(partials, 8 * n, "partial sums")
+    _need(out, 8, "output")
+    _check("zero_sum_partials", library().zero_sum_partials(
+        _ptr(partials), n, _ptr(out), 1 if accumulate else 0, _stream(stream)))
 
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0,

@@ -195,6 +195,22 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
                       void* d_workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * zero_sum_partials -- the combine of a bucketed sum of squares: *d_out = the
+ * sum of the n doubles at d_partials (or *d_out += it when accumulate != 0),
+ * in an order that depends only on n, so equal inputs give bit-identical
+ * results whatever order or streams produced the partials. A shard processed
+ * in constant-size buckets (notes on the ZeRO paper, section 5.2, constant
+ * buffer size; "ZeRO-3 核心流程", the prefetch bucket) can write each bucket's
+ * sum of squares to its own slot, on any stream, and combine the slots once
+ * every bucket is done.
+ *   d_partials  device array of n doubles
+ *   d_out       device pointer to one double (not inside d_partials)
+ * Errors: ZERO_EINVAL for n < 0, a NULL d_out, or a NULL d_partials with
+ * n > 0; ZERO_EHIP if the launch fails. n == 0 writes 0 (or leaves *d_out
+ * unchanged when accumulating). */
+int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_t accumulate, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Layout of the fp32 optimizer state (12 bytes per element: master, m, v).
  * The state of an n-element shard is ONE buffer of 3*n floats in tiles of
  * ZERO_STATE_TILE elements. Tile k covers elements [k*T, k*T + L_k) with

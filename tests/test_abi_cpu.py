@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     lib = zero.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -138,6 +138,10 @@ def test_device_calls_reject_bad_arguments_on_the_host():
     assert lib.zero_accumulate_grads(None, None, -1, 0, None) == zero.ZERO_EINVAL
     assert lib.zero_accumulate_grads(None, None, 4, 0, None) == zero.ZERO_EINVAL
     assert lib.zero_shard_sqnorm_f32(None, 4, None, 0, None, 0, None) == zero.ZERO_EINVAL
+    assert lib.zero_sum_partials(None, -1, None, 0, None) == zero.ZERO_EINVAL
+    assert lib.zero_sum_partials(None, 3, ctypes.c_void_p(8), 0, None) == zero.ZERO_EINVAL   # NULL partials
+    assert lib.zero_sum_partials(ctypes.c_void_p(8), 3, None, 0, None) == zero.ZERO_EINVAL   # NULL output
+    assert lib.zero_sum_partials(ctypes.c_void_p(12), 3, ctypes.c_void_p(8), 0, None) == zero.ZERO_EINVAL
     assert lib.zero_adamw_step_f32grad(None, None, None, 8, 0, 8, ctypes.byref(hp), None, 1,
                                        None) == zero.ZERO_EINVAL
     assert lib.zero_state_export(None, None, None, None, 5, None) == zero.ZERO_EINVAL

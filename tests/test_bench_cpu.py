@@ -112,6 +112,33 @@ def test_stats_summary_table(tmp_path):
     assert float(adamw[7]) == pytest.approx(100 * 28 * S / 2e-6 / 1e9 / 8000, abs=0.1)
     assert int(table["copy_pieces_kernel<false>"][5]) == 4 * S
     assert table["sqnorm_final_kernel"][5] == "-"
+    assert adamw[8] == "-"                        # no kernel trace: no busy time
+
+
+def test_stats_summary_busy_time_is_the_union_of_launches(tmp_path):
+    """Launches on two streams overlap: the busy time per step is the union
+    of the launch intervals, and the rate over it counts each byte once."""
+    wl = synth.WORKLOADS["tiny"]
+    S = 262_144
+    ns = "(anonymous namespace)::"
+    adamw = f"void {ns}adamw_vec_kernel<unsigned short>({ns}AdamWArgs)"
+    final = f"{ns}sqnorm_final_kernel(double const*, long, double*, int)"
+    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+               [{"Name": adamw, "Calls": 4, "AverageNs": 2000, "MinNs": 2000, "MaxNs": 2000},
+                {"Name": final, "Calls": 2, "AverageNs": 100, "MinNs": 100, "MaxNs": 100}])
+    # two steps; in each, two 2 us launches overlapping by 1 us (3 us busy)
+    trace = []
+    for t0 in (0, 10_000):
+        trace += [{"Kernel_Name": adamw, "Start_Timestamp": t0, "End_Timestamp": t0 + 2000},
+                  {"Kernel_Name": adamw, "Start_Timestamp": t0 + 1000, "End_Timestamp": t0 + 3000},
+                  {"Kernel_Name": final, "Start_Timestamp": t0 + 5000, "End_Timestamp": t0 + 5100}]
+    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_trace.csv"),
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
+    md = bench.stats_summary(str(tmp_path / "prof"), wl, steps=2, warmup=0, flat=True)
+    row = [line for line in md.splitlines() if line.startswith("| adamw_vec_kernel")][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    assert float(cells[9]) == pytest.approx(3.0)                        # busy us per step
+    assert float(cells[10]) == pytest.approx(28 * S / 3e-6 / 1e9, abs=0.1)
 
 
 def _counter_csvs(tmp_path, raw):

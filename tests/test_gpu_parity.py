@@ -332,6 +332,31 @@ def test_sqnorm_exact_special_values():
     assert np.isinf(inf)
 
 
+@pytest.mark.parametrize("n", [0, 1, 2, 7, 173, 1000, 250_001])
+def test_sum_partials(n):
+    """The combine of bucket sums: the oracle's sum (rank order) and the
+    exactly rounded sum agree with the GPU's fixed-order sum to n ulps; exact
+    on integer values; bit-identical when repeated; additive when
+    accumulating."""
+    import math
+    rng = np.random.default_rng(n + 5)
+    x = rng.random(n) * 10.0 ** rng.integers(-6, 3, n).astype(np.float64)   # nine decades
+    d = torch.from_numpy(x).to(DEV)
+    out = torch.full((1,), 7.0, dtype=torch.float64, device=DEV)
+    zero.zero_sum_partials(d, n, out, False)
+    got = float(out.cpu()[0])
+    exact = math.fsum(x)
+    assert abs(got - exact) <= max(n, 1) * 2.0 ** -52 * exact
+    assert abs(got - O.global_sqnorm(x)) <= max(n, 1) * 2.0 ** -51 * exact
+    zero.zero_sum_partials(d, n, out, False)
+    assert float(out.cpu()[0]) == got
+    zero.zero_sum_partials(d, n, out, True)
+    assert float(out.cpu()[0]) == got + got
+    ints = rng.integers(0, 1 << 20, n).astype(np.float64)                     # sums exact in fp64
+    zero.zero_sum_partials(torch.from_numpy(ints).to(DEV), n, out, False)
+    assert float(out.cpu()[0]) == float(ints.sum())
+
+
 def test_sqnorm_rejects_small_workspace():
     g = to_dev_u16(np.zeros(10_000_000, np.uint16))
     out = torch.zeros(1, dtype=torch.float64, device=DEV)

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 
 def bits(t):
-    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+    """The tensor's bits as integers of its element size."""
+    return t.view({2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()])
 
 
 def test_two_streams_equal_sequential_steps():
@@ -33,9 +34,25 @@ def test_two_streams_equal_sequential_steps():
         torch.cuda.synchronize()
         for name, a, b in zip(names, concurrent, sequential):
             for buf in ("state", "param_shard", "grad_shard", "rank_sq"):
-                x, y = getattr(a, buf), getattr(b, buf)
-                same = torch.equal(x.view(torch.int64), y.view(torch.int64)) if x.dtype == torch.float64 else \
-                    torch.equal(bits(x), bits(y))
-                assert same, (name, k, buf)
+                assert torch.equal(bits(getattr(a, buf)), bits(getattr(b, buf))), (name, k, buf)
             for i in a.touched:
                 assert torch.equal(bits(a.params[i]), bits(b.params[i])), (name, k, i)
+
+
+def test_bucketed_step_on_one_or_two_streams():
+    """A bucketed step (each bucket's sum of squares in its own slot, one
+    fixed-order combine, the buckets dealt out to the streams) gives the same
+    bits on one stream and on two, over several steps."""
+    wl = synth.WORKLOADS["gpt2-1.5b"]
+    one = RankShard(wl, bucket=5_000_000, streams=1)
+    two = RankShard(wl, bucket=5_000_000, streams=2)
+    assert one.bucketed and two.bucketed and one.n_streams == 1 and two.n_streams == 2
+    for k in range(3):
+        print(f"[buckets] step {k}", flush=True)
+        one.step(wl.step + k)
+        two.step(wl.step + k)
+        torch.cuda.synchronize()
+        for buf in ("state", "param_shard", "grad_shard", "bucket_sq", "rank_sq"):
+            assert torch.equal(bits(getattr(one, buf)), bits(getattr(two, buf))), (k, buf)
+        for i in one.touched:
+            assert torch.equal(bits(one.params[i]), bits(two.params[i])), (k, i)

@@ -141,12 +141,15 @@ def test_workload_full_size(name, fused_norm, bucket, fused_unpack):
     rel = assert_norm_close(got, want, f"{name} partial")
     print(f"[{name}] partial sum of squares: relative error of sqrt {rel:.2e}", flush=True)
     again = torch.zeros(1, dtype=torch.float64, device="cuda")
-    for k, (b, n) in enumerate(rs.pieces()):
-        if fused_norm:
-            zero.zero_pack_grads_sqnorm(rs.layout, rs.grads, rs.grad_shard, b, n, again, k > 0,
-                                        rs.workspace)
-        else:
-            zero.zero_shard_sqnorm(rs.grad_shard[b:], n, again, k > 0, rs.workspace)
+    if rs.bucketed:                                      # bucket slots, then the fixed-order combine
+        rs.pack_norm_buckets(again, torch.cuda.current_stream())
+    else:
+        for k, (b, n) in enumerate(rs.pieces()):
+            if fused_norm:
+                zero.zero_pack_grads_sqnorm(rs.layout, rs.grads, rs.grad_shard, b, n, again, k > 0,
+                                            rs.workspace)
+            else:
+                zero.zero_shard_sqnorm(rs.grad_shard[b:], n, again, k > 0, rs.workspace)
     assert float(again.cpu()) == got                     # bit-identical repeat
 
     # AdamW on the sampled ranges
