@@ -142,7 +142,7 @@ def one_trial(rng, trial):
         assert (whole[:PAD + off] == synth.SENTINEL).all() and (whole[PAD + off + sizes[i]:] == synth.SENTINEL).all()
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_layouts(seed):
     rng = np.random.default_rng(1000 + seed)
     for k in range(10):
