@@ -79,11 +79,11 @@ def oracle_partial(grad_shard, S):
 
 
 # (workload, fused norm, bucket, fused unpack): bucket None keeps the
-# workload's own bucketing. The 70B shard in one piece makes a single AdamW
-# launch of 2.2e9 four-element units, more than its 2^23-block grid holds, so
-# that launch strides; the fused pack then covers 8.6e9 elements in two
-# launches and its final sum adds ~1e6 block partials. The 7B shard's 75
-# segments take two launches of the fused update.
+# workload's own bucketing. The 70B shard in one piece is updated in 65
+# launches of equal length (at most 2^27 elements each); the fused pack then
+# covers 8.6e9 elements in two launches (91 pieces, 64 per launch) and its
+# final sum adds ~1e6 block partials. The 7B shard's 1.68e9 elements take 13
+# update launches.
 FULL_SIZE = ([(n, f, None, True) for n in ("gpt2-1.5b", "gpt-7.5b", "llama-7b", "llama-70b") for f in (True, False)]
              + [("llama-70b", True, 0, True), ("gpt-7.5b", True, None, False), ("llama-7b", True, None, False)])
 
