@@ -55,9 +55,19 @@ inline float widen(uint16_t h) {
   return x;
 }
 
+// Clones of the inner loop for AVX-512 and AVX2+FMA, chosen at load time.
+// Compilers that take no x86-64-v3/v4 clone targets (GCC before 12) build
+// the baseline loop only: std::fma is then a correctly rounded library call,
+// so the results are the same, only slower.
+#if defined(__clang__) || (defined(__GNUC__) && __GNUC__ >= 12)
+#define ZERO_HOST_CLONES __attribute__((target_clones("arch=x86-64-v4", "arch=x86-64-v3", "default")))
+#else
+#define ZERO_HOST_CLONES
+#endif
+
 // One contiguous run of n elements: gradients g[0..n), state slots p/m/v
 // (stride 1), parameters out[0..n).
-__attribute__((target_clones("arch=x86-64-v4", "arch=x86-64-v3", "default")))
+ZERO_HOST_CLONES
 void adam_run(const HostAdam& a, const uint16_t* __restrict g, float* __restrict p, float* __restrict m,
               float* __restrict v, uint16_t* __restrict out, int64_t n) {
   for (int64_t j = 0; j < n; ++j) {
