@@ -205,8 +205,8 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
  * every bucket is done.
  *   d_partials  device array of n doubles
  *   d_out       device pointer to one double (not inside d_partials)
- * Errors: ZERO_EINVAL for n < 0, a NULL d_out, or a NULL d_partials with
- * n > 0; ZERO_EHIP if the launch fails. n == 0 writes 0 (or leaves *d_out
+ * Errors: ZERO_EINVAL for n < 0, a NULL d_out, a NULL d_partials with n > 0,
+ * or a pointer that is not 8-byte aligned; ZERO_EHIP if the launch fails. n == 0 writes 0 (or leaves *d_out
  * unchanged when accumulating). */
 int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_t accumulate, hipStream_t stream);
 
