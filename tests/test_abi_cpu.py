@@ -74,6 +74,21 @@ def test_layout_matches_oracle_random():
             _compare(sizes, n_d, rank, align)
 
 
+def test_layout_matches_oracle_many_ranks():
+    """Large data-parallel degrees and alignments: shards shorter than a
+    tensor, ranks made wholly of padding, alignment beyond the model size."""
+    rng = np.random.default_rng(100)
+    for _ in range(100):
+        t = int(rng.integers(1, 50))
+        sizes = [int(x) for x in rng.integers(0, 1_000_000, size=t)]
+        if sum(sizes) == 0:
+            sizes[0] = 7
+        n_d = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000))]))
+        align = int(rng.choice([1, 64, 256, 4096, 1 << 20]))
+        for rank in {0, n_d - 1, int(rng.integers(0, n_d)), n_d // 2}:
+            _compare(sizes, n_d, rank, align)
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_layout_matches_oracle_workloads(name):
     wl = synth.WORKLOADS[name]
