@@ -230,10 +230,15 @@ struct Piece {
   int64_t len;
 };
 
-// A launch's work-item count must fit in 32 bits: at most 2^23 blocks of 256.
-constexpr int64_t kCopyMaxBlocksPerLaunch = int64_t(1) << 23;
-// Pieces are cut to at most 2^34 elements (2^21 blocks) so any piece fits.
+// A launch's work-item count must fit in 32 bits: at most 2^31 lanes, so
+// 2^23 blocks of the plain copy and 2^22 of the copy with the sum of squares.
+constexpr int64_t kCopyMaxLanesPerLaunch = int64_t(1) << 31;
+// Pieces are cut to at most 2^34 elements (2^23 plain-copy blocks, 2^21 with
+// the sum of squares) so any piece fits one launch.
 constexpr int64_t kCopyMaxPieceElems = int64_t(1) << 34;
+static_assert(kCopyMaxPieceElems / (kCopyVecPerBlock * 8) <= kCopyMaxLanesPerLaunch / kCopyThreads &&
+                  kCopyMaxPieceElems / kCopySqElemPerBlock <= kCopyMaxLanesPerLaunch / kCopySqThreads,
+              "a piece of the maximum length fits one launch");
 
 // Launches copying `pieces`, batched by kCopyMaxPieces and by the block limit.
 // With `partial` non-NULL the sum-of-squares variant runs and each block writes
@@ -241,6 +246,7 @@ constexpr int64_t kCopyMaxPieceElems = int64_t(1) << 34;
 int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who,
                   double* partial = nullptr, int64_t* n_partial = nullptr) {
   const int64_t per_block = partial ? kCopySqVecPerBlock : kCopyVecPerBlock;
+  const int64_t max_blocks = kCopyMaxLanesPerLaunch / (partial ? kCopySqThreads : kCopyThreads);
   size_t i = 0;
   int64_t done = 0;
   while (i < pieces.size()) {
@@ -252,7 +258,7 @@ int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const ch
       const bool vec = pc.src == nullptr ||
                        ((uintptr_t(pc.src) & 15u) == (uintptr_t(pc.dst) & 15u));
       const int64_t nb = copy_blocks(pc.dst, pc.len, vec, per_block);
-      if (n > 0 && blocks + nb > kCopyMaxBlocksPerLaunch) break;  // launch what we have first
+      if (n > 0 && blocks + nb > max_blocks) break;  // launch what we have first
       P.src[n] = pc.src;
       P.dst[n] = pc.dst;
       P.len[n] = pc.len;
@@ -262,7 +268,7 @@ int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const ch
     }
     P.n = n;
     P.first_block[n] = blocks;
-    if (blocks > kCopyMaxBlocksPerLaunch) return fail(ZERO_EINVAL, "%s: piece too large for one launch", who);
+    if (blocks > max_blocks) return fail(ZERO_EINVAL, "%s: piece too large for one launch", who);
     // slot table: the smallest power-of-two run of blocks that needs at most
     // kCopySlots slots, and for each slot the piece holding its first block
     int shift = 0;
