@@ -215,11 +215,12 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
                       "traffic_over_algorithmic": round(bytes_ / per_dispatch[k], 4) if k in per_dispatch else None}
     return {"workload": wl.name, "rank": wl.rank, "shard": S,
             "commands": [
-                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline",
-                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o bench -- "
-                f"python3 bench.py --workload {wl.name} {mode} --no-cpu-baseline",
-                f"python bench.py --workload {wl.name} {mode} --pmc-summary {fetch_dir} {write_dir}"],
+                "cd /tmp && export TMPDIR=/tmp   # R: the repository root",
+                f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/{fetch_dir} -o bench -- "
+                f"python3 $R/bench.py --workload {wl.name} {mode} --no-cpu-baseline",
+                f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/{write_dir} -o bench -- "
+                f"python3 $R/bench.py --workload {wl.name} {mode} --no-cpu-baseline",
+                f"cd $R && python bench.py --workload {wl.name} {mode} --pmc-summary {fetch_dir} {write_dir}"],
             "counter_units": "KiB per dispatch, averaged over dispatches",
             "kernel_code_sha256": source_hash(),
             "calibration": {"kernel": copy, "source": source, "known_read_kib": known_kib,
@@ -263,11 +264,12 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
             (" --flat" if flat else "") + (" --separate-unpack" if separate_unpack else ""))
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
              f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
-             "Command (repository root, one MI355X):", "",
-             f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o bench -- "
-             f"python3 bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
+             "Commands (one MI355X; R is the repository root):", "",
+             "    cd /tmp && export TMPDIR=/tmp",
+             f"    timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d $R/{stats_dir} -o bench -- "
+             f"python3 $R/bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
              f"--no-cpu-baseline --no-copy-ceiling",
-             f"    python bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
+             f"    cd $R && python bench.py --workload {wl.name} --steps {steps} --warmup {warmup}{mode} "
              f"--stats-summary {stats_dir}", "",
              f"kernels.hip code sha256 (comments and blank space aside): `{source_hash()}`", "",
              f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "

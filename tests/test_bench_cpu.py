@@ -171,7 +171,7 @@ def test_pmc_summary_calibration_from_the_copy_ceiling(tmp_path):
     assert out["kernels"][update]["algorithmic_bytes"] == 30 * S
     assert out["kernels"][update]["traffic_over_algorithmic"] == pytest.approx(1.0)
     assert out["kernels"]["copy_pieces_kernel<true>"]["traffic_over_algorithmic"] == pytest.approx(1.0)
-    assert "--no-copy-ceiling" not in out["commands"][0]
+    assert "--no-copy-ceiling" not in out["commands"][1] and "TMPDIR" in out["commands"][0]
 
 
 @needs_lib
@@ -191,7 +191,7 @@ def test_pmc_summary_calibration(tmp_path):
     assert a["algorithmic_bytes"] == 28 * S
     assert a["traffic_bytes"] == pytest.approx(14 * S + 14 * S * 1.01, rel=1e-6)
     assert a["traffic_over_algorithmic"] == pytest.approx(1.005, abs=1e-4)
-    assert "--steps 3 --warmup 2" in out["commands"][0]
+    assert "--steps 3 --warmup 2" in out["commands"][1]
     json.dumps(out)
 
 
