@@ -40,8 +40,13 @@ def test_edge_classes():
 
 
 def test_random_patterns():
+    """10^8 random 32-bit patterns, in chunks of 2^24."""
     rng = np.random.default_rng(7)
-    _check(rng.integers(0, 2**32, size=4_000_000, dtype=np.uint64).astype(np.uint32))
+    left = 100_000_000
+    while left > 0:
+        n = min(left, 1 << 24)
+        _check(rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32))
+        left -= n
 
 
 def test_all_low_halves_of_some_exponents():
