@@ -163,9 +163,10 @@ class RankShard:
         return [(b, min(self.bucket, self.shard - b)) for b in range(0, self.shard, self.bucket)]
 
     def step(self, step, stream=None, timing=None, events=None, before_micro=None, phases=None):
-        """One local step. ``timing``: optional dict; each phase ("pack_sqnorm"
-        or "pack" and "sqnorm", "adamw", "unpack") gets a list of (start, end)
-        CUDA events recorded around its launches on the current stream, taken
+        """One local step on ``stream`` (a torch stream or a raw handle; by
+        default the current stream). ``timing``: optional dict; each phase
+        ("pack_sqnorm" or "pack" and "sqnorm", "adamw", "unpack") gets a list
+        of (start, end) CUDA events recorded around its launches on that stream, taken
         from the iterator ``events`` (pre-created, so timing adds no event
         creation to the step); ``phases`` limits the timed phases (each event
         record costs GPU time between launches). A bucketed default step times
@@ -180,7 +181,9 @@ class RankShard:
                                timing, events, phases)
             return
         if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
+            stream = torch.cuda.current_stream()
+        on = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream   # events go here
+        stream = on.cuda_stream
 
         def mark(phase, fn):
             if timing is None or (phases is not None and phase not in phases):
@@ -188,9 +191,9 @@ class RankShard:
                 return
             e0 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
             e1 = next(events) if events is not None else torch.cuda.Event(enable_timing=True)
-            e0.record()
+            e0.record(on)
             fn()
-            e1.record()
+            e1.record(on)
             timing.setdefault(phase, []).append((e0, e1))
 
         if self.accum_steps > 1:
