@@ -1,7 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times (RankShard.step: whole shard, or 5e7-element buckets for the
 70B shard). The oracle checks sampled ranges element by element; the rank's
-whole-shard sum of squares is recomputed by the oracle over the full shard.
+whole-shard sum of squares is recomputed by the oracle over the full shard,
+packed by the oracle from the per-tensor gradients.
 
 Per workload:
   * pack: sampled shard ranges equal the oracle's pack of the same ranges of
@@ -61,14 +62,15 @@ def sample_ranges(lay, wl, rng):
     return sorted((s, c) for s in starts)
 
 
-def oracle_partial(grad_shard, S):
-    """The oracle's sum of squares of the whole device shard, streamed to the
-    host in pieces (summed in order)."""
+def oracle_partial(lay, tensors, S):
+    """The oracle's sum of squares of the rank's whole shard: the oracle packs
+    it from the per-tensor gradients (the inputs, fetched in pieces) and sums
+    each piece's squares; the pieces' sums are added in order."""
     piece = 1 << 27
     bounds = [(lo, min(S, lo + piece)) for lo in range(0, S, piece)]
 
     def one(b):
-        return O.sqnorm(u16(grad_shard[b[0]:b[1]]))
+        return O.sqnorm(O.pack(lay, tensors, b[0], b[1] - b[0]))
 
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         parts = list(ex.map(one, bounds))
@@ -137,7 +139,7 @@ def test_workload_full_size(name, fused_norm, bucket, fused_unpack):
 
     # sum of squares over the whole shard
     got = float(rs.rank_sq[rs.rank].cpu())
-    want = oracle_partial(rs.grad_shard, S)
+    want = oracle_partial(lay, lazy, S)
     rel = assert_norm_close(got, want, f"{name} partial")
     print(f"[{name}] partial sum of squares: relative error of sqrt {rel:.2e}", flush=True)
     again = torch.zeros(1, dtype=torch.float64, device="cuda")
