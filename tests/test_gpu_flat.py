@@ -17,7 +17,7 @@ def u16(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("name,rank", [("tiny", 1), ("tiny", 3), ("gpt2-1.5b", 63), ("gpt-7.5b", 1)])
+@pytest.mark.parametrize("name,rank", [("tiny", 1), ("tiny", 3), ("gpt2-1.5b", 63), ("gpt-7.5b", 1), ("llama-7b", 3)])
 def test_flat_equals_packed(name, rank):
     from fsdp_sharded_mixed_zero_amd.rank import RankShard
 
