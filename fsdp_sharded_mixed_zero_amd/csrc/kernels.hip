@@ -1056,11 +1056,10 @@ template <typename G>
 static int adamw_args(const G* d_grad, float* d_state, uint16_t* d_param, int64_t n_state, int64_t begin,
                       int64_t count, const zero_adamw_hparams* hp, const double* d_rank_sqnorms, int32_t n_ranks,
                       const char* who, AdamWArgs* out, bool* vec) {
-  if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
+  if (int rc = zero::check_adamw_hparams(hp, who)) return rc;
   if (n_state < 0 || begin < 0 || count < 0 || begin > n_state || count > n_state - begin)
     return fail(ZERO_EINVAL, "%s: range [%lld, +%lld) outside a state of %lld elements", who, (long long)begin,
                 (long long)count, (long long)n_state);
-  if (hp->step < 1) return fail(ZERO_EINVAL, "%s: step must be >= 1 (got %lld)", who, (long long)hp->step);
   const bool clip = hp->max_norm > 0.0;
   if (clip && (d_rank_sqnorms == nullptr || n_ranks < 1))
     return fail(ZERO_EINVAL, "%s: clipping needs the ranks' sums of squares", who);

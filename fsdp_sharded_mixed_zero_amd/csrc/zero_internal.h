@@ -21,4 +21,21 @@ int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Clear the calling thread's message and return ZERO_OK.
 int ok();
 
+// The hyperparameter checks of every update entry point (GPU and host):
+// step >= 1, and the argument rules of PyTorch's AdamW (lr >= 0, eps >= 0,
+// 0 <= beta1, beta2 < 1, weight_decay >= 0), plus clip_eps >= 0. A NaN fails
+// them. max_norm is free: <= 0 (or NaN) turns clipping off.
+inline int check_adamw_hparams(const zero_adamw_hparams* hp, const char* who) {
+  if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
+  if (hp->step < 1) return fail(ZERO_EINVAL, "%s: step must be >= 1 (got %lld)", who, (long long)hp->step);
+  if (!(hp->lr >= 0.0)) return fail(ZERO_EINVAL, "%s: invalid learning rate %g", who, hp->lr);
+  if (!(hp->eps >= 0.0)) return fail(ZERO_EINVAL, "%s: invalid eps %g", who, hp->eps);
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO_EINVAL, "%s: beta1 %g outside [0, 1)", who, hp->beta1);
+  if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO_EINVAL, "%s: beta2 %g outside [0, 1)", who, hp->beta2);
+  if (!(hp->weight_decay >= 0.0))
+    return fail(ZERO_EINVAL, "%s: invalid weight decay %g", who, hp->weight_decay);
+  if (!(hp->clip_eps >= 0.0)) return fail(ZERO_EINVAL, "%s: invalid clip_eps %g", who, hp->clip_eps);
+  return ZERO_OK;
+}
+
 }  // namespace zero

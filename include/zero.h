@@ -263,7 +263,9 @@ int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_
  * longer than 2^27 elements is updated in several equal launches on `stream`
  * (each element once; the results do not depend on the split).
  * Errors: ZERO_EINVAL for null pointers (all may be NULL when count == 0), a
- * range outside [0, n_state), step < 1, n_ranks < 1 with clipping on;
+ * range outside [0, n_state), n_ranks < 1 with clipping on, or hyperparameters
+ * that PyTorch's AdamW refuses (lr, eps or weight_decay below 0, a beta
+ * outside [0, 1); a NaN fails these checks), clip_eps below 0 or step < 1;
  * ZERO_EHIP if a launch fails. Non-finite inputs propagate per IEEE rules (a
  * NaN norm gives a NaN coefficient). */
 int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,

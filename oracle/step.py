@@ -47,6 +47,9 @@ CHUNK = 1 << 22   # elements per piece: temporaries stay a constant size
 
 @dataclass(frozen=True)
 class AdamWHParams:
+    """Hyperparameters, refused as ``torch.optim.AdamW`` refuses them (lr,
+    eps and weight_decay below 0, a beta outside [0, 1); NaN fails every
+    check), and clip_eps below 0. max_norm is free: <= 0 turns clipping off."""
     lr: float = 1e-3
     beta1: float = 0.9
     beta2: float = 0.999
@@ -54,6 +57,20 @@ class AdamWHParams:
     weight_decay: float = 0.01
     max_norm: float = 1.0
     clip_eps: float = 1e-6
+
+    def __post_init__(self):
+        if not self.lr >= 0.0:
+            raise ValueError(f"invalid learning rate {self.lr}")
+        if not self.eps >= 0.0:
+            raise ValueError(f"invalid eps {self.eps}")
+        for name in ("beta1", "beta2"):
+            b = getattr(self, name)
+            if not 0.0 <= b < 1.0:
+                raise ValueError(f"{name} {b} outside [0, 1)")
+        if not self.weight_decay >= 0.0:
+            raise ValueError(f"invalid weight decay {self.weight_decay}")
+        if not self.clip_eps >= 0.0:
+            raise ValueError(f"invalid clip_eps {self.clip_eps}")
 
 
 # ---------------------------------------------------------------- pack/unpack

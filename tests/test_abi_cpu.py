@@ -174,6 +174,50 @@ def test_device_calls_reject_bad_arguments_on_the_host():
         assert fn(None, None, None, 128, 3, 0, ctypes.byref(off), None, 0, lay.handle, arr, None) == zero.ZERO_OK
 
 
+def test_device_calls_reject_invalid_hyperparameters():
+    """What torch.optim.AdamW refuses (and clip_eps below 0) the GPU updates
+    refuse on the host, before anything is launched."""
+    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS
+
+    lib = zero.library()
+    n = 8
+    fake = ctypes.c_void_p(1 << 20)                  # never dereferenced: the checks fail first
+    lay = zero.zero_layout([n], 1, 0, 1)
+    ptrs = zero.pointer_array([None])
+    for kw in INVALID_HPARAMS + [dict(clip_eps=-1e-6)]:
+        hp = zero.hparams(**kw)
+        for fn in (lib.zero_adamw_step, lib.zero_adamw_step_f32grad):
+            assert fn(fake, fake, fake, n, 0, n, ctypes.byref(hp), fake, 1, None) == zero.ZERO_EINVAL, kw
+        for fn in (lib.zero_adamw_step_unpack, lib.zero_adamw_step_f32grad_unpack):
+            assert fn(fake, fake, fake, n, 0, n, ctypes.byref(hp), fake, 1, lay.handle, ptrs,
+                      None) == zero.ZERO_EINVAL, kw
+        assert zero.zero_last_error()
+    for kw in EDGE_HPARAMS:                          # accepted (an empty range launches nothing)
+        hp = zero.hparams(**kw)
+        assert lib.zero_adamw_step(fake, fake, fake, n, 0, 0, ctypes.byref(hp), fake, 1, None) == zero.ZERO_OK
+
+
+def test_cpu_update_refuses_invalid_hyperparameters():
+    """The host update applies the same checks."""
+    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS
+
+    lib = zero.library()
+    n = 8
+    h_grad = (ctypes.c_uint16 * n)()
+    h_state = (ctypes.c_float * (3 * n))()
+    h_param = (ctypes.c_uint16 * n)()
+    parts = (ctypes.c_double * 1)(1.0)
+    for kw in INVALID_HPARAMS + [dict(clip_eps=-1e-6)]:
+        hp = zero.hparams(**kw)
+        assert lib.zero_cpu_adamw_step(h_grad, h_state, h_param, n, 0, n, ctypes.byref(hp), parts, 1,
+                                       1) == zero.ZERO_EINVAL, kw
+        assert zero.zero_last_error()
+    for kw in EDGE_HPARAMS:
+        hp = zero.hparams(**kw)
+        assert lib.zero_cpu_adamw_step(h_grad, h_state, h_param, n, 0, n, ctypes.byref(hp), parts, 1,
+                                       1) == zero.ZERO_OK, kw
+
+
 def test_empty_ranges_return_before_any_launch():
     """An update over an empty range is a no-op that returns OK on the host
     (no launch, no division by its length), at the start, inside and at the

@@ -310,3 +310,38 @@ def test_adamw_f32grad_agrees_with_bf16_path():
     p1, m1, _, _ = S.adamw_step_f32grad(g, master, np.zeros(n, np.float32), np.zeros(n, np.float32),
                                         1, S.AdamWHParams(weight_decay=0.0, max_norm=0.0), 1.0)
     assert np.array_equal(m1, (0.1 * g.astype(np.float64)).astype(np.float32))
+
+
+# ------------------------------------------------------- argument checking
+
+INVALID_HPARAMS = [dict(lr=-1e-3), dict(lr=float("nan")), dict(eps=-1e-8), dict(eps=float("nan")),
+                   dict(beta1=-0.1), dict(beta1=1.0), dict(beta2=1.0), dict(beta2=1.5), dict(beta2=float("nan")),
+                   dict(weight_decay=-0.01), dict(weight_decay=float("nan"))]
+EDGE_HPARAMS = [dict(lr=0.0), dict(eps=0.0), dict(beta1=0.0), dict(beta2=0.0), dict(weight_decay=0.0),
+                dict(lr=float("inf"))]
+
+
+def _torch_adamw(kw):
+    p = torch.nn.Parameter(torch.zeros(3, dtype=torch.float64))
+    return torch.optim.AdamW([p], lr=kw.get("lr", 1e-3), betas=(kw.get("beta1", 0.9), kw.get("beta2", 0.999)),
+                             eps=kw.get("eps", 1e-8), weight_decay=kw.get("weight_decay", 0.01))
+
+
+@pytest.mark.parametrize("kw", INVALID_HPARAMS)
+def test_hparams_refused_as_torch_refuses_them(kw):
+    with pytest.raises(ValueError):
+        _torch_adamw(kw)
+    with pytest.raises(ValueError):
+        S.AdamWHParams(**kw)
+
+
+@pytest.mark.parametrize("kw", EDGE_HPARAMS)
+def test_hparams_accepted_as_torch_accepts_them(kw):
+    _torch_adamw(kw)
+    S.AdamWHParams(**kw)
+
+
+def test_clip_eps_below_zero_refused():
+    with pytest.raises(ValueError):
+        S.AdamWHParams(clip_eps=-1e-6)
+    S.AdamWHParams(clip_eps=0.0, max_norm=float("nan"))    # max_norm is free
