@@ -446,6 +446,21 @@ def test_adamw_steps_and_ranks(step, n_ranks):
         _check_adamw(*_adamw_case(n, 0, n, step, ohp, n_ranks, 1e-4, 1e-8, seed=step + n_ranks))
 
 
+EDGE_UPDATES = [dict(beta1=0.0), dict(beta2=0.0), dict(beta1=0.0, beta2=0.0), dict(lr=0.0), dict(eps=0.0),
+                dict(weight_decay=0.0), dict(weight_decay=1.0), dict(beta1=0.999999, beta2=0.999999)]
+
+
+@pytest.mark.parametrize("kw", EDGE_UPDATES, ids=[",".join(f"{k}={v}" for k, v in kw.items()) for kw in EDGE_UPDATES])
+@pytest.mark.parametrize("step", [1, 2])
+def test_adamw_edge_hyperparameters(kw, step):
+    """Hyperparameters at the ends of their allowed ranges: no momentum, no
+    second-moment averaging, no step, no eps, no decay, strong decay, betas
+    next to 1 (bias corrections near 0)."""
+    ohp = O.AdamWHParams(**kw)
+    n = 10_000 + 3
+    _check_adamw(*_adamw_case(n, 0, n, step, ohp, 2, 1e-4, 1e-8, seed=17 + step))
+
+
 def test_adamw_first_step_from_zero_state():
     # m = v = 0 at step 1: the update is lr * g' / (|g'| + eps) (+ decay)
     ohp = O.AdamWHParams()

@@ -72,6 +72,17 @@ def test_cpu_adamw_hyperparameters(step):
         _case(50_000, 0, 50_000, step, ohp, 8, 2, seed=step)
 
 
+EDGE_UPDATES = [dict(beta1=0.0), dict(beta2=0.0), dict(beta1=0.0, beta2=0.0), dict(lr=0.0), dict(eps=0.0),
+                dict(weight_decay=0.0), dict(weight_decay=1.0), dict(beta1=0.999999, beta2=0.999999)]
+
+
+@pytest.mark.parametrize("kw", EDGE_UPDATES, ids=[",".join(f"{k}={v}" for k, v in kw.items()) for kw in EDGE_UPDATES])
+def test_cpu_adamw_edge_hyperparameters(kw):
+    """The ends of the allowed ranges, as on the GPU."""
+    for step in (1, 2):
+        _case(10_003, 0, 10_003, step, O.AdamWHParams(**kw), 2, 2, seed=17 + step)
+
+
 def test_cpu_adamw_threads_agree():
     # the split across threads does not change any bit
     outs = [_case(1_000_003, 0, 1_000_003, 5, O.AdamWHParams(), 4, t, seed=5) for t in (1, 3, 8, 0)]
