@@ -23,8 +23,8 @@ int ok();
 
 // The hyperparameter checks of every update entry point (GPU and host):
 // step >= 1, and the argument rules of PyTorch's AdamW (lr >= 0, eps >= 0,
-// 0 <= beta1, beta2 < 1, weight_decay >= 0), plus clip_eps >= 0. A NaN fails
-// them. max_norm is free: <= 0 (or NaN) turns clipping off.
+// 0 <= beta1, beta2 < 1, weight_decay >= 0), plus clip_eps >= 0 and a
+// max_norm that is a number (<= 0 turns clipping off). A NaN fails them all.
 inline int check_adamw_hparams(const zero_adamw_hparams* hp, const char* who) {
   if (hp == nullptr) return fail(ZERO_EINVAL, "%s: NULL hyperparameters", who);
   if (hp->step < 1) return fail(ZERO_EINVAL, "%s: step must be >= 1 (got %lld)", who, (long long)hp->step);
@@ -35,6 +35,7 @@ inline int check_adamw_hparams(const zero_adamw_hparams* hp, const char* who) {
   if (!(hp->weight_decay >= 0.0))
     return fail(ZERO_EINVAL, "%s: invalid weight decay %g", who, hp->weight_decay);
   if (!(hp->clip_eps >= 0.0)) return fail(ZERO_EINVAL, "%s: invalid clip_eps %g", who, hp->clip_eps);
+  if (hp->max_norm != hp->max_norm) return fail(ZERO_EINVAL, "%s: max_norm is NaN", who);
   return ZERO_OK;
 }
 

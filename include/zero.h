@@ -86,9 +86,9 @@ typedef struct {
 
 /* AdamW hyperparameters. `step` is the 1-based step count used for the bias
  * corrections 1-beta1^step and 1-beta2^step (computed on the host in fp64).
- * max_norm <= 0 turns clipping off; otherwise the gradient is scaled by
- * c = max_norm / (sqrt(G) + clip_eps) when that is below 1, G being the global
- * sum of squares. */
+ * max_norm <= 0 turns clipping off (NaN is refused); otherwise the gradient
+ * is scaled by c = max_norm / (sqrt(G) + clip_eps) when that is below 1, G
+ * being the global sum of squares. */
 typedef struct {
   double lr;
   double beta1;
@@ -265,7 +265,8 @@ int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_
  * Errors: ZERO_EINVAL for null pointers (all may be NULL when count == 0), a
  * range outside [0, n_state), n_ranks < 1 with clipping on, or hyperparameters
  * that PyTorch's AdamW refuses (lr, eps or weight_decay below 0, a beta
- * outside [0, 1); a NaN fails these checks), clip_eps below 0 or step < 1;
+ * outside [0, 1); a NaN fails these checks), clip_eps below 0, a NaN
+ * max_norm or step < 1;
  * ZERO_EHIP if a launch fails. Non-finite inputs propagate per IEEE rules (a
  * NaN norm gives a NaN coefficient). */
 int zero_adamw_step(const uint16_t* d_grad, float* d_state, uint16_t* d_param, int64_t n_state,

@@ -49,7 +49,8 @@ CHUNK = 1 << 22   # elements per piece: temporaries stay a constant size
 class AdamWHParams:
     """Hyperparameters, refused as ``torch.optim.AdamW`` refuses them (lr,
     eps and weight_decay below 0, a beta outside [0, 1); NaN fails every
-    check), and clip_eps below 0. max_norm is free: <= 0 turns clipping off."""
+    check), and clip_eps below 0 or a NaN max_norm. A max_norm <= 0 turns
+    clipping off."""
     lr: float = 1e-3
     beta1: float = 0.9
     beta2: float = 0.999
@@ -71,6 +72,8 @@ class AdamWHParams:
             raise ValueError(f"invalid weight decay {self.weight_decay}")
         if not self.clip_eps >= 0.0:
             raise ValueError(f"invalid clip_eps {self.clip_eps}")
+        if math.isnan(self.max_norm):
+            raise ValueError("max_norm is NaN")
 
 
 # ---------------------------------------------------------------- pack/unpack

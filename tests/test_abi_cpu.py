@@ -175,16 +175,17 @@ def test_device_calls_reject_bad_arguments_on_the_host():
 
 
 def test_device_calls_reject_invalid_hyperparameters():
-    """What torch.optim.AdamW refuses (and clip_eps below 0) the GPU updates
-    refuse on the host, before anything is launched."""
-    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS
+    """What torch.optim.AdamW refuses (and clip_eps below 0 or a NaN
+    max_norm) the GPU updates refuse on the host, before anything is
+    launched."""
+    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS, OWN_INVALID
 
     lib = zero.library()
     n = 8
     fake = ctypes.c_void_p(1 << 20)                  # never dereferenced: the checks fail first
     lay = zero.zero_layout([n], 1, 0, 1)
     ptrs = zero.pointer_array([None])
-    for kw in INVALID_HPARAMS + [dict(clip_eps=-1e-6)]:
+    for kw in INVALID_HPARAMS + OWN_INVALID:
         hp = zero.hparams(**kw)
         for fn in (lib.zero_adamw_step, lib.zero_adamw_step_f32grad):
             assert fn(fake, fake, fake, n, 0, n, ctypes.byref(hp), fake, 1, None) == zero.ZERO_EINVAL, kw
@@ -199,7 +200,7 @@ def test_device_calls_reject_invalid_hyperparameters():
 
 def test_cpu_update_refuses_invalid_hyperparameters():
     """The host update applies the same checks."""
-    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS
+    from test_oracle_step import EDGE_HPARAMS, INVALID_HPARAMS, OWN_INVALID
 
     lib = zero.library()
     n = 8
@@ -207,7 +208,7 @@ def test_cpu_update_refuses_invalid_hyperparameters():
     h_state = (ctypes.c_float * (3 * n))()
     h_param = (ctypes.c_uint16 * n)()
     parts = (ctypes.c_double * 1)(1.0)
-    for kw in INVALID_HPARAMS + [dict(clip_eps=-1e-6)]:
+    for kw in INVALID_HPARAMS + OWN_INVALID:
         hp = zero.hparams(**kw)
         assert lib.zero_cpu_adamw_step(h_grad, h_state, h_param, n, 0, n, ctypes.byref(hp), parts, 1,
                                        1) == zero.ZERO_EINVAL, kw

@@ -341,7 +341,14 @@ def test_hparams_accepted_as_torch_accepts_them(kw):
     S.AdamWHParams(**kw)
 
 
-def test_clip_eps_below_zero_refused():
+OWN_INVALID = [dict(clip_eps=-1e-6), dict(clip_eps=float("nan")), dict(max_norm=float("nan"))]
+
+
+@pytest.mark.parametrize("kw", OWN_INVALID)
+def test_clip_arguments_refused(kw):
+    """The clip arguments (not torch.optim.AdamW's): clip_eps below 0 and a
+    NaN max_norm are refused; max_norm <= 0 or infinite is allowed."""
     with pytest.raises(ValueError):
-        S.AdamWHParams(clip_eps=-1e-6)
-    S.AdamWHParams(clip_eps=0.0, max_norm=float("nan"))    # max_norm is free
+        S.AdamWHParams(**kw)
+    for ok in (dict(clip_eps=0.0), dict(max_norm=0.0), dict(max_norm=-1.0), dict(max_norm=float("inf"))):
+        S.AdamWHParams(**ok)
