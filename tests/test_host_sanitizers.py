@@ -69,3 +69,33 @@ def test_host_code_built_with_gcc(tmp_path):
                        timeout=900)
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
     assert " passed" in r.stdout
+
+
+def test_sanitizer_catches_a_planted_overrun(tmp_path):
+    """The harness above would pass just as well if the sanitizer never fired:
+    a host library built the same way, with a one-element heap overrun, must
+    abort the child with AddressSanitizer's report."""
+    if not os.path.exists(CLANG):
+        pytest.skip("ROCm clang++ not found")
+    runtime = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                             text=True).stdout.strip()
+    if not os.path.isabs(runtime) or not os.path.exists(runtime):
+        pytest.skip("sanitizer runtime not found")
+    src = tmp_path / "overrun.cpp"
+    src.write_text("#include <vector>\n"
+                   "extern \"C\" int overrun(int n) {\n"
+                   "  std::vector<int> v(n, 1);\n"
+                   "  int s = 0;\n"
+                   "  for (int i = 0; i <= n; ++i) s += v.data()[i];   // one past the end\n"
+                   "  return s;\n"
+                   "}\n")
+    lib = str(tmp_path / "liboverrun.so")
+    r = subprocess.run([CLANG, "-shared", "-fPIC", "-O1", "-g", "-fno-omit-frame-pointer",
+                        "-fsanitize=address,undefined", "-shared-libsan", "-std=c++17", str(src), "-o", lib],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, LD_PRELOAD=runtime, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    r = subprocess.run([sys.executable, "-c", f"import ctypes; print(ctypes.CDLL({lib!r}).overrun(8))"],
+                       env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "heap-buffer-overflow" in r.stderr, r.stderr[-3000:]
