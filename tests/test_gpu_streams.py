@@ -56,3 +56,26 @@ def test_bucketed_step_on_one_or_two_streams():
             assert torch.equal(bits(getattr(one, buf)), bits(getattr(two, buf))), (k, buf)
         for i in one.touched:
             assert torch.equal(bits(one.params[i]), bits(two.params[i])), (k, i)
+
+
+def test_step_on_a_given_stream_times_its_own_launches():
+    """A step handed a stream (a torch stream or its raw handle) runs there
+    and records its timing events there: each phase's interval covers its
+    kernels (the GPT-2 shard's update moves 0.73 GB, so it takes tens of
+    microseconds at least), and the results equal a step on the current
+    stream bit for bit."""
+    wl = synth.WORKLOADS["gpt2-1.5b"]
+    side, ref = RankShard(wl), RankShard(wl)
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for k, handle in enumerate((st, st.cuda_stream)):
+        print(f"[given stream] step {k}", flush=True)
+        timing = {}
+        side.step(wl.step + k, stream=handle, timing=timing)
+        ref.step(wl.step + k)
+        torch.cuda.synchronize()
+        for phase in ("pack_sqnorm", "adamw"):
+            (e0, e1), = timing[phase]
+            assert e0.elapsed_time(e1) * 1e3 > (50.0 if phase == "adamw" else 5.0), (phase, e0.elapsed_time(e1))
+        for buf in ("state", "param_shard", "grad_shard", "rank_sq"):
+            assert torch.equal(bits(getattr(side, buf)), bits(getattr(ref, buf))), (k, buf)
