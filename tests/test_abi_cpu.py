@@ -352,3 +352,45 @@ def test_binding_refuses_short_buffers():
     # an empty range reaches nothing
     zero.zero_cpu_adamw_step(np.zeros(0, np.uint16), np.zeros(0, np.float32), np.zeros(0, np.uint16), n, 5, 0,
                              hp, None, 0)
+
+
+def test_last_error_is_per_thread():
+    """zero_last_error() reports the calling thread's own last failure: two
+    threads fail in different ways at the same time, and a third that
+    succeeds sees an empty message."""
+    import threading
+
+    lib = zero.library()
+    barrier = threading.Barrier(3)
+    seen = {}
+
+    def fail_layout():
+        h = ctypes.c_void_p()
+        arr = (ctypes.c_int64 * 2)(4, 4)
+        barrier.wait()
+        for _ in range(200):
+            assert lib.zero_layout(arr, 2, 0, 0, 1, ctypes.byref(h)) == zero.ZERO_EINVAL   # n_d = 0
+        seen["layout"] = zero.zero_last_error()
+
+    def fail_update():
+        hp = zero.hparams(step=0)
+        g, st, p = (ctypes.c_uint16 * 8)(), (ctypes.c_float * 24)(), (ctypes.c_uint16 * 8)()
+        barrier.wait()
+        for _ in range(200):
+            assert lib.zero_cpu_adamw_step(g, st, p, 8, 0, 8, ctypes.byref(hp), None, 0, 1) == zero.ZERO_EINVAL
+        seen["update"] = zero.zero_last_error()
+
+    def succeed():
+        barrier.wait()
+        for _ in range(200):
+            zero.zero_layout([8, 8], 2, 1, 1)
+        seen["ok"] = zero.zero_last_error()
+
+    threads = [threading.Thread(target=f) for f in (fail_layout, fail_update, succeed)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert "zero_layout" in seen["layout"] and "zero_cpu_adamw_step" not in seen["layout"]
+    assert "zero_cpu_adamw_step" in seen["update"] and "zero_layout" not in seen["update"]
+    assert seen["ok"] == ""
