@@ -176,3 +176,31 @@ def test_fused_update_across_launch_cuts(f32grad):
             for i, (x, y) in enumerate(zip(t0, t1)):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (rank, b, c, i)
             del outs, s0, s1
+
+
+def test_element_path_across_launch_cuts():
+    """A gradient pointer off its vector alignment sends every launch down the
+    element path; over a range of three launches it must give the vector
+    path's bits, for the update and for the update with the unpack fused."""
+    S = 2 * CUT + 3 * TILE + 5
+    grad, state0 = make_state(S, False, seed=9)
+    shifted = torch.empty(S + 1, dtype=torch.bfloat16, device=DEV)[1:]
+    shifted.copy_(grad)
+    assert shifted.data_ptr() % 8 == 2
+    parts = torch.tensor([2.0, 3.0], dtype=torch.float64, device=DEV)
+    hp = zero.hparams(max_norm=1.0, step=4)
+    lay = zero.zero_layout([S], 1, 0, 1)
+    outs = []
+    for g in (grad, shifted):
+        print(f"[element path] gradient at {g.data_ptr() % 16} mod 16", flush=True)
+        state, param = state0.clone(), torch.zeros(S, dtype=torch.bfloat16, device=DEV)
+        zero.zero_adamw_step(g, state, param, S, 0, S, hp, parts, 2)
+        f_state, f_param = state0.clone(), torch.zeros(S, dtype=torch.bfloat16, device=DEV)
+        tensor = torch.zeros(S, dtype=torch.bfloat16, device=DEV)
+        zero.zero_adamw_step_unpack(g, f_state, f_param, S, 0, S, hp, parts, 2, lay, [tensor])
+        torch.cuda.synchronize()
+        outs.append((state, param, f_state, f_param, tensor))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int32 if a.dtype == torch.float32 else torch.int16),
+                           b.view(torch.int32 if b.dtype == torch.float32 else torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[0][4].view(torch.int16))
