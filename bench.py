@@ -23,7 +23,8 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, AMD's published peak
-EVENT_EVERY = 8               # timed steps per step with events around AdamW
+BREAKDOWN_MIN_STEPS = 100     # steps with events around every phase, before the timed region
+BREAKDOWN_MIN_SECONDS = 1.0   # ... and at least this much wall time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_zero_amd", "csrc", "kernels.hip")
@@ -63,6 +64,12 @@ def parse():
                     help="summarise a rocprofv3 --kernel-trace --stats run of this benchmark "
                          "(kernel durations, achieved GB/s) as markdown and exit")
     return ap.parse_args()
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
 # ---------------------------------------------------------------- HBM traffic
@@ -610,54 +617,56 @@ def main():
                    fused_unpack=not args.separate_unpack)
     torch.cuda.synchronize()
 
+    # Per-phase breakdown first, outside the timed region: events around every
+    # phase of each step, for at least BREAKDOWN_MIN_STEPS steps and
+    # BREAKDOWN_MIN_SECONDS of wall time. Besides the per-kernel table and the
+    # roofline (the median update launch), this keeps the GPU busy long
+    # enough to reach its steady clocks before the timed steps: an idle GPU
+    # starts a short run ~10% slower.
     t = wl.step
+    n_p = len(rs.pieces())
+    per_step = 2 * (n_p * (2 if args.separate_norm else 1) + 2 * n_p + (3 * args.accum + 1) * n_p)
+    phase_timing = {}
+    breakdown_steps = 0
+    t0 = time.perf_counter()
+    while breakdown_steps < BREAKDOWN_MIN_STEPS or time.perf_counter() - t0 < BREAKDOWN_MIN_SECONDS:
+        batch = 10
+        events = iter([torch.cuda.Event(enable_timing=True) for _ in range(per_step * batch)])
+        for _ in range(batch):
+            rs.step(t, timing=phase_timing, events=events)
+            t += 1
+        breakdown_steps += batch
+        torch.cuda.synchronize()
+
+    # the timed region: W warm-up steps, then exactly K steps, nothing else
     for _ in range(args.warmup):
         rs.step(t)
         t += 1
     torch.cuda.synchronize()
-    # timed region: events around the AdamW launches (the roofline kernel) of
-    # every EVENT_EVERY-th step only. Each event record costs ~3 us of GPU time
-    # between launches (0.8% of the 7.5B step for one pair), which would
-    # otherwise be charged to every step.
-    n_p = len(rs.pieces())
-    per_step = 2 * (n_p * (2 if args.separate_norm else 1) + 2 * n_p + (3 * args.accum + 1) * n_p)
-    timed_steps = list(range(0, args.steps, EVENT_EVERY))
-    timing = {}
-    events = iter([torch.cuda.Event(enable_timing=True) for _ in range(2 * n_p * len(timed_steps))])
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i % EVENT_EVERY == 0:
-            rs.step(t, timing=timing, events=events, phases=("adamw",))
-        else:
-            rs.step(t)
+    for _ in range(args.steps):
+        rs.step(t)
         t += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    # untimed breakdown: events around every phase
-    breakdown_steps = min(args.steps, 50)
-    phase_timing = {}
-    events = iter([torch.cuda.Event(enable_timing=True) for _ in range(per_step * breakdown_steps)])
-    for _ in range(breakdown_steps):
-        rs.step(t, timing=phase_timing, events=events)
-        t += 1
-    torch.cuda.synchronize()
 
     ms_per_step = wall * 1e3 / args.steps
     S = rs.shard
     algo = rs.bytes_per_step()
     kernels = {}
     for phase, evs in phase_timing.items():
-        per_step_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / breakdown_steps
-        launches = len(evs) / breakdown_steps
+        launches = len(evs) // breakdown_steps
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        per_step_ms = median([sum(ms[k * launches:(k + 1) * launches]) for k in range(breakdown_steps)])
         gbps = algo[phase] / (per_step_ms * 1e-3) / 1e9
         kernels[phase] = {"us_per_step": round(per_step_ms * 1e3, 2), "launches_per_step": launches,
                           "algorithmic_bytes": algo[phase], "GBps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
     # each event pair spans one update call: one kernel launch unless the
     # call's range needs several (then the pair spans them all, back to back)
-    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in timing["adamw"]) / len(timing["adamw"])
-    calls = len(timing["adamw"]) / len(timed_steps)
+    call_times = sorted(e0.elapsed_time(e1) for e0, e1 in phase_timing["adamw"])
+    call_ms = median(call_times)
+    calls = len(call_times) / breakdown_steps
     call_elems = S / calls
     call_bytes = algo["adamw"] / calls
     achieved = call_bytes / (call_ms * 1e-3) / 1e9
@@ -696,15 +705,20 @@ def main():
         "adamw_params_per_s": call_elems / (call_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
-        "kernels_note": f"per-phase times from {breakdown_steps} further steps with events around every "
-                        f"phase (outside the timed region)",
+        "kernels_note": f"median per-step time of each phase over {breakdown_steps} steps with events around "
+                        f"every phase, run before the warm-up (outside the timed region)",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
     unit, units = ("phase", "phases") if bucketed else ("launch", "launches") if single else ("call", "calls")
     out["roofline"].update({
-        f"algorithmic_bytes_per_{unit}": int(call_bytes), f"timed_{units}": len(timing["adamw"]),
-        "events": f"around the AdamW {units} of every {EVENT_EVERY}th step of the timed region"})
+        f"algorithmic_bytes_per_{unit}": int(call_bytes), f"timed_{units}": len(call_times),
+        "statistic": f"median {unit} duration",
+        f"us_per_{unit}": {"median": round(call_ms * 1e3, 2),
+                           "p10": round(call_times[len(call_times) // 10] * 1e3, 2),
+                           "p90": round(call_times[(9 * len(call_times)) // 10] * 1e3, 2)},
+        "events": f"a HIP event pair on the update's stream around each AdamW {unit} of the "
+                  f"{breakdown_steps} breakdown steps"})
     if bucketed:
         out["roofline"]["note"] = (f"the update phase: one launch per bucket, the buckets dealt out to {n_streams} "
                                    f"streams; achieved is the phase's bytes over its time")
