@@ -5,10 +5,11 @@
 // results travel back over PCIe; "別再複製本可分片的東西" mentions CPU and NVMe
 // offload of the sharded state).
 //
-// The update is the same fp32 operation sequence as the GPU kernel (fused
+// The update is the same operation sequence as the GPU kernel (fp32 with fused
 // multiply-adds, correctly rounded square root and division, round-to-nearest-
-// even bf16 cast), on the same tiled state layout, so the offloaded step and
-// the GPU step agree bit for bit on hosts with hardware FMA. Work is split
+// even bf16 cast; the same cancellation test and fp64 recomputation of the
+// elements it flags), on the same tiled state layout, so the offloaded step
+// and the GPU step agree bit for bit on hosts with hardware FMA. Work is split
 // across threads by whole elements ranges; each thread walks the tiles its
 // range meets and runs a contiguous, vectorisable loop per tile. The inner
 // loop is compiled for AVX-512, AVX2+FMA and baseline x86-64 and picked at run
@@ -39,7 +40,28 @@ constexpr int64_t kTile = ZERO_STATE_TILE;
 
 struct HostAdam {
   float beta1, omb1, beta2, omb2, lr_wd, step_size, inv_sqrt_bc2, eps, coef;
+  double coef64;         // the clip coefficient before its rounding to fp32
+  zero::AdamWExact x;    // the constants in fp64, for the exact recomputation
 };
+
+// The GPU kernel's cancellation test: elements whose new master is below
+// kCancel times the size of the terms it is formed from are recomputed in
+// fp64 (see adamw_exact).
+constexpr float kCancel = 0x1p-12f;
+
+// One element recomputed from its old values in fp64 IEEE arithmetic, in
+// PyTorch AdamW's order; m', v', p' are stored as their fp32 roundings.
+inline void adam_exact(const HostAdam& a, float g, float& p, float& m, float& v) {
+  const zero::AdamWExact& x = a.x;
+  const double gh = a.coef64 * double(g);
+  const double m1 = x.beta1 * double(m) + x.omb1 * gh;
+  const double v1 = x.beta2 * double(v) + x.omb2 * (gh * gh);
+  const double denom = std::sqrt(v1) / x.sqrt_bc2 + x.eps;
+  const double p1 = double(p) * x.decay - x.step_size * (m1 / denom);
+  p = float(p1);
+  m = float(m1);
+  v = float(v1);
+}
 
 inline uint16_t bf16_rne(float x) {
   uint32_t u;
@@ -71,15 +93,23 @@ ZERO_HOST_CLONES
 void adam_run(const HostAdam& a, const uint16_t* __restrict g, float* __restrict p, float* __restrict m,
               float* __restrict v, uint16_t* __restrict out, int64_t n) {
   for (int64_t j = 0; j < n; ++j) {
-    const float gh = widen(g[j]) * a.coef;
-    const float mj = std::fma(a.beta1, m[j], a.omb1 * gh);
+    const float gj = widen(g[j]);
+    const float gh = gj * a.coef;
+    const float mg = a.omb1 * gh;
+    const float mj = std::fma(a.beta1, m[j], mg);
     const float vj = std::fma(a.beta2, v[j], a.omb2 * (gh * gh));
     const float denom = std::fma(std::sqrt(vj), a.inv_sqrt_bc2, a.eps);
-    const float pj = std::fma(-a.step_size, mj / denom, std::fma(-a.lr_wd, p[j], p[j]));
-    m[j] = mj;
-    v[j] = vj;
-    p[j] = pj;
-    out[j] = bf16_rne(pj);
+    const float pd = std::fma(-a.lr_wd, p[j], p[j]);
+    const float pj = std::fma(-a.step_size, mj / denom, pd);
+    if (std::fma(-kCancel, std::fabs(pd), std::fabs(pj)) * denom <
+        (kCancel * a.step_size) * (std::fabs(a.beta1 * m[j]) + std::fabs(mg))) {
+      adam_exact(a, gj, p[j], m[j], v[j]);
+    } else {
+      m[j] = mj;
+      v[j] = vj;
+      p[j] = pj;
+    }
+    out[j] = bf16_rne(p[j]);
   }
 }
 
@@ -218,7 +248,9 @@ int cpu_adamw(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t
   a.step_size = float(hp->lr / (1.0 - std::pow(hp->beta1, t)));
   a.inv_sqrt_bc2 = float(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
   a.eps = float(hp->eps);
+  zero::adamw_exact_constants(hp, &a.x);
   a.coef = 1.0f;
+  a.coef64 = 1.0;
   if (clip) {
     // the GPU update's order: lane sums of ranks l, l+64, l+128, ... (each in
     // rank order), then the 64 lane sums in order (for at most 64 ranks, the
@@ -230,7 +262,8 @@ int cpu_adamw(const uint16_t* h_grad, float* h_state, uint16_t* h_param, int64_t
       G2 += run;
     }
     const double ratio = hp->max_norm / (std::sqrt(G2) + hp->clip_eps);
-    a.coef = float(ratio >= 1.0 ? 1.0 : ratio);   // a NaN ratio stays NaN
+    a.coef64 = ratio >= 1.0 ? 1.0 : ratio;   // a NaN ratio stays NaN
+    a.coef = float(a.coef64);
   }
 
   int64_t threads = n_threads > 0 ? n_threads : usable_cpus();

@@ -240,14 +240,21 @@ int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_
  * section 3; notes on the ZeRO paper, section 4.1), K = 12 bytes of fp32
  * state per parameter (section 2 of the lesson; notes section 2.1).
  * Per element, with g the bf16 gradient widened to fp32:
- *   c  = clip coefficient from G = d_rank_sqnorms[0] + ... + d_rank_sqnorms[n_ranks-1]
+ *   c  = clip coefficient max_norm / (sqrt(G) + clip_eps), capped at 1, in
+ *        fp64, from G = d_rank_sqnorms[0] + ... + d_rank_sqnorms[n_ranks-1]
  *        in fp64, in a fixed order: for at most 64 ranks, rank order; beyond,
  *        64 lane sums (lane l adds ranks l, l+64, l+128, ... in order), then
  *        the lane sums in lane order
  *   g' = c*g;  m = beta1*m + (1-beta1)*g';  v = beta2*v + (1-beta2)*g'^2
  *   master = master*(1 - lr*wd) - (lr/(1-beta1^t)) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
  *   param  = bf16 round-to-nearest-even of the new fp32 master
- * Arithmetic is fp32 with correctly rounded division and square root.
+ * Arithmetic is fp32 (c rounded to fp32) with correctly rounded division and
+ * square root, except where the new master comes out below 2^-12 of the
+ * magnitudes it is formed from (cancellation; ~2e-5 of the elements): such
+ * an element is recomputed from its old values in fp64 IEEE arithmetic in the
+ * order above, and stored as the fp32 roundings of the fp64 results. Every
+ * bf16 parameter is then within one bf16 step of the rounding of the exactly
+ * computed master.
  *   d_grad    device pointer to the bf16 gradient shard's element 0
  *   d_state   device pointer to the tiled fp32 state of all n_state elements
  *             (layout above); updated in place
@@ -366,7 +373,8 @@ int zero_unpack_params(zero_layout_t h, const uint16_t* param_shard, uint16_t* c
  * over PCIe; "別再複製本可分片的東西": CPU offload of the sharded state).
  * Same update, state layout and arithmetic as zero_adamw_step (fp32 with fused
  * multiply-adds, correctly rounded sqrt and division, round-to-nearest-even
- * bf16), so on hosts with hardware FMA it matches the GPU bit for bit.
+ * bf16; the same cancellation test and fp64 recomputation), so on hosts with
+ * hardware FMA it matches the GPU bit for bit.
  *   h_grad    HOST array of the count bf16 gradients of the range (element
  *             begin first): a staging buffer the caller fills from the GPU
  *   h_state   HOST pointer to the tiled fp32 state of all n_state elements

@@ -576,3 +576,53 @@ def test_adamw_f32grad_sub_ranges(begin, count):
     n = 3 * TILE + 10
     _check_adamw(*_adamw_case(n, begin, count, 2, O.AdamWHParams(), 2, 1e-4, 1e-8,
                               seed=begin + count, f32grad=True))
+
+
+# ------------------------------------------------------------ cancellation
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("fused", [False, True])
+def test_update_cancellation(kind, fused):
+    """Masters planted at cancellation points (a tenth of 2^20 + 77 elements):
+    every bf16 parameter within 1 ulp of the oracle's; the elements whose exact
+    new master is below 2^-14 of its terms (recomputed in fp64) equal to the
+    oracle's fp32 values bit for bit; the others within 2^-21 of the terms;
+    and the same bits as the host update. ``fused``: the update with the
+    unpack, over a one-tensor layout."""
+    from cancellation_inputs import planted
+    from oracle.bf16 import bf16_to_f32
+
+    n = (1 << 20) + 77
+    bits, master, m, v, step, G, deep, size = planted(n, 9, kind)
+    ohp = O.AdamWHParams()
+    hp = hp_of(ohp, step)
+    st0 = to_tiles(master, m, v)
+    d_state = to_dev_f32(st0)
+    d_param = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    rs = torch.tensor([G], dtype=torch.float64, device=DEV)
+    if fused:
+        h = zero.zero_layout([n], 1, 0, 1)
+        d_t = sentinel(n)
+        zero.zero_adamw_step_unpack(to_dev_u16(bits), d_state, d_param, n, 0, n, hp, rs, 1, h, [d_t])
+    else:
+        zero.zero_adamw_step(to_dev_u16(bits), d_state, d_param, n, 0, n, hp, rs, 1)
+    g_state = d_state.cpu().numpy()
+    g_param = to_host_u16(d_param)
+    if fused:
+        assert np.array_equal(to_host_u16(d_t), g_param)
+    h_state = st0.copy()
+    h_param = np.zeros(n, np.uint16)
+    zero.zero_cpu_adamw_step(bits, h_state, h_param, n, 0, n, hp, np.array([G]), 1, 4)
+    assert np.array_equal(g_state.view(np.uint32), h_state.view(np.uint32)), "GPU and host state differ"
+    assert np.array_equal(g_param, h_param), "GPU and host parameters differ"
+    coef = O.clip_coef(G, ohp.max_norm, ohp.clip_eps)
+    want = O.adamw_step(bits, master, m, v, step, ohp, coef)
+    exact = O.adamw_f64(master, m, v, coef * bf16_to_f32(bits).astype(np.float64), step, ohp)[0]
+    g_master, g_m, g_v = from_tiles(g_state, n)
+    assert deep.sum() > 1000
+    assert (np.abs(g_master - exact) <= 2.0 ** -21 * size).all()
+    assert_f32_state(g_m, want[1], "m", m)
+    assert_f32_state(g_v, want[2], "v", v)
+    assert_bf16_param(g_param, want[3], want[0], "param", g_master)
+    for name, got, exp in (("master", g_master, want[0]), ("m", g_m, want[1]), ("v", g_v, want[2])):
+        assert np.array_equal(got[deep].view(np.uint32), exp[deep].view(np.uint32)), name

@@ -9,6 +9,7 @@ import pytest
 
 from fsdp_sharded_mixed_zero_amd import synth, zero
 from oracle import step as O
+from oracle.bf16 import bf16_to_f32
 from state_tiles import TILE, from_tiles, to_tiles
 from tolerance import assert_bf16_param, assert_f32_state
 
@@ -209,3 +210,30 @@ def test_cpu_adamw_concurrent_callers():
     for k in range(4):
         assert np.array_equal(together[k][0].view(np.uint32), alone[k][0].view(np.uint32)), k
         assert np.array_equal(together[k][1], alone[k][1]), k
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_cpu_adamw_cancellation(kind):
+    """Masters planted at cancellation points (a tenth of 2^20 elements): every
+    bf16 parameter within 1 ulp of the oracle's, and the elements whose exact
+    new master is below 2^-14 of its terms (recomputed in fp64) equal to the
+    oracle's fp32 values bit for bit."""
+    from cancellation_inputs import planted
+
+    n = 1 << 20
+    bits, master, m, v, step, G, deep, size = planted(n, 5, kind)
+    ohp = O.AdamWHParams()
+    state = to_tiles(master, m, v)
+    param = np.zeros(n, np.uint16)
+    zero.zero_cpu_adamw_step(bits, state, param, n, 0, n, _hp(ohp, step), np.array([G]), 1, 4)
+    coef = O.clip_coef(G, ohp.max_norm, ohp.clip_eps)
+    want = O.adamw_step(bits, master, m, v, step, ohp, coef)
+    exact = O.adamw_f64(master, m, v, coef * bf16_to_f32(bits).astype(np.float64), step, ohp)[0]
+    g_master, g_m, g_v = from_tiles(state, n)
+    assert deep.sum() > 1000
+    assert (np.abs(g_master - exact) <= 2.0 ** -21 * size).all()
+    assert_f32_state(g_m, want[1], "m", m)
+    assert_f32_state(g_v, want[2], "v", v)
+    assert_bf16_param(param, want[3], want[0], "param", g_master)
+    for name, got, exp in (("master", g_master, want[0]), ("m", g_m, want[1]), ("v", g_v, want[2])):
+        assert np.array_equal(got[deep].view(np.uint32), exp[deep].view(np.uint32)), name

@@ -2,11 +2,10 @@
 
   * layout, offsets, packed/unpacked bf16 bytes: bit-exact;
   * fp32 master, m, v: |gpu - oracle| <= 1e-8 + 1e-6 * |oracle|;
-  * bf16 parameters: at most 1 bf16 ulp apart (ordered-integer distance), or,
-    where the oracle's fp32 master is so close to zero that the fp32 rule's
-    tolerance interval spans more bf16 values, at most as far as the bf16
-    images of that interval's ends; and each GPU parameter is exactly the
-    round-to-nearest-even bf16 of the GPU's own fp32 master (torch's cast);
+  * bf16 parameters: at most 1 bf16 ulp apart (ordered-integer distance),
+    everywhere, near-zero masters included; and each GPU parameter is
+    exactly the round-to-nearest-even bf16 of the GPU's own fp32 master
+    (torch's cast);
   * global norm: |sqrt(G_gpu) - sqrt(G_oracle)| <= 1e-5 * sqrt(G_oracle).
 
 The fp32 rule's absolute term (1e-8) exceeds typical v values (~1e-9 to 1e-12),
@@ -15,7 +14,6 @@ so fp32 state is also bounded in ulps of |old| + |new| (see assert_f32_state).
 
 import numpy as np
 
-from oracle.bf16 import f32_to_bf16
 
 RTOL_F32 = 1e-6
 ATOL_F32 = 1e-8
@@ -74,21 +72,18 @@ def assert_bf16_close(got_bits, want_bits, name, max_ulp=1):
 
 
 def assert_bf16_param(got_bits, want_bits, want_master, name, got_master=None):
-    """bf16 parameters against the oracle's (see the module docstring). The
-    allowance comes from oracle values only: the fp32 rule's interval around
-    the oracle's master, rounded outward to fp32, then to bf16."""
-    want_master = np.asarray(want_master, np.float32)
-    w = want_master.astype(np.float64)
-    tol = ATOL_F32 + RTOL_F32 * np.abs(w)
-    hi = np.nextafter((w + tol).astype(np.float32), np.float32(np.inf))
-    lo = np.nextafter((w - tol).astype(np.float32), np.float32(-np.inf))
+    """bf16 parameters against the oracle's: at most 1 bf16 ulp apart at every
+    element (``want_master``, the oracle's fp32 master, is named in the
+    failure message), and, when ``got_master`` is given, each parameter is the
+    round-to-nearest-even bf16 of its own fp32 master. Returns the largest
+    distance."""
     ow = ordered_bf16(want_bits)
-    allow = np.maximum.reduce([np.ones_like(ow), ordered_bf16(f32_to_bf16(hi)) - ow,
-                               ow - ordered_bf16(f32_to_bf16(lo))])
     d = np.abs(ordered_bf16(got_bits) - ow)
-    bad = d > allow
-    assert not bad.any(), (f"{name}: {int(d[bad].max())} bf16 ulp apart (allowed {int(allow[bad][0])}) "
-                           f"at {np.flatnonzero(bad)[:5]}")
+    bad = d > 1
+    if bad.any():
+        k = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{name}: {int(d.max())} bf16 ulp apart at {k} "
+                             f"(oracle masters {np.asarray(want_master, np.float32)[k]})")
     if got_master is not None:
         import torch
         cast = torch.from_numpy(np.ascontiguousarray(got_master, np.float32)).to(torch.bfloat16)
