@@ -31,9 +31,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "zero_internal.h"
@@ -244,17 +246,17 @@ static_assert(kCopyMaxPieceElems / (kCopyVecPerBlock * 8) <= kCopyMaxLanesPerLau
 // Launches copying `pieces`, batched by kCopyMaxPieces and by the block limit.
 // With `partial` non-NULL the sum-of-squares variant runs and each block writes
 // partial[k] (k counts blocks across all launches); *n_partial gets the count.
-int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who,
+int launch_pieces(const Piece* pieces, size_t n_pieces, hipStream_t stream, const char* who,
                   double* partial = nullptr, int64_t* n_partial = nullptr) {
   const int64_t per_block = partial ? kCopySqVecPerBlock : kCopyVecPerBlock;
   const int64_t max_blocks = kCopyMaxLanesPerLaunch / (partial ? kCopySqThreads : kCopyThreads);
   size_t i = 0;
   int64_t done = 0;
-  while (i < pieces.size()) {
+  while (i < n_pieces) {
     CopyPieces P{};
     int64_t blocks = 0;
     int n = 0;
-    for (; i < pieces.size() && n < kCopyMaxPieces; ++i, ++n) {
+    for (; i < n_pieces && n < kCopyMaxPieces; ++i, ++n) {
       const Piece& pc = pieces[i];
       const bool vec = pc.src == nullptr ||
                        ((uintptr_t(pc.src) & 15u) == (uintptr_t(pc.dst) & 15u));
@@ -292,6 +294,11 @@ int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const ch
   }
   if (n_partial) *n_partial = done;
   return zero::ok();
+}
+
+int launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who,
+                  double* partial = nullptr, int64_t* n_partial = nullptr) {
+  return launch_pieces(pieces.data(), pieces.size(), stream, who, partial, n_partial);
 }
 
 // Upper bound of the blocks the sum-of-squares copy uses for pieces of these
@@ -338,6 +345,74 @@ int build_pieces(const zero_layout_s* h, uint16_t* const* tensors, uint16_t* sha
   }
   return zero::ok();
 }
+
+// The pieces of shard range [begin, begin+count), produced a batch at a time
+// into the caller's storage: the pieces build_pieces lists, in its order,
+// without allocating memory.
+class PieceCursor {
+ public:
+  PieceCursor(const zero_layout_s* h, uint16_t* const* tensors, uint16_t* shard, int64_t begin, int64_t count,
+              bool to_shard)
+      : h_(h), tensors_(tensors), shard_(shard), begin_(begin), end_(begin + count), to_shard_(to_shard) {
+    const auto& segs = h->segs;
+    s_ = size_t(std::upper_bound(segs.begin(), segs.end(), begin,
+                                 [](int64_t v, const zero_segment& g) { return v < g.dst_off + g.len; }) -
+                segs.begin());
+    a_ = begin;
+  }
+
+  // Fills up to `cap` pieces; returns how many (0 once the range is done), or
+  // a negative error code for a tensor pointer the range needs that is NULL or
+  // misaligned.
+  int64_t next(Piece* out, int64_t cap, const char* who) {
+    const auto& segs = h_->segs;
+    int64_t n = 0;
+    while (n < cap) {
+      if (!in_pad_) {
+        if (s_ >= segs.size() || segs[s_].dst_off >= end_) {
+          in_pad_ = true;
+          a_ = std::max(h_->info.pad_begin, begin_);
+          continue;
+        }
+        const zero_segment& g = segs[s_];
+        const int64_t lo = std::max(g.dst_off, begin_), hi = std::min(g.dst_off + g.len, end_);
+        if (a_ < lo) a_ = lo;
+        if (a_ >= hi) {
+          ++s_;
+          continue;
+        }
+        uint16_t* t = tensors_[g.tensor];
+        if (t == nullptr)
+          return fail(ZERO_EINVAL, "%s: pointer of tensor %lld is NULL but the range needs it", who,
+                      (long long)g.tensor);
+        if (uintptr_t(t) & 1u)
+          return fail(ZERO_EINVAL, "%s: tensor %lld pointer is not 2-byte aligned", who, (long long)g.tensor);
+        const int64_t len = std::min(kCopyMaxPieceElems, hi - a_);
+        uint16_t* tp = t + g.src_off + (a_ - g.dst_off);
+        uint16_t* sp = shard_ + a_;
+        out[n++] = to_shard_ ? Piece{tp, sp, len} : Piece{sp, tp, len};
+        a_ += len;
+      } else {
+        const int64_t hi = std::min(h_->info.pad_end, end_);
+        if (!to_shard_ || a_ >= hi) return n;   // unpack: padding goes nowhere
+        const int64_t len = std::min(kCopyMaxPieceElems, hi - a_);
+        out[n++] = Piece{nullptr, shard_ + a_, len};
+        a_ += len;
+      }
+    }
+    return n;
+  }
+
+ private:
+  const zero_layout_s* h_;
+  uint16_t* const* tensors_;
+  uint16_t* shard_;
+  int64_t begin_, end_;
+  bool to_shard_;
+  size_t s_ = 0;          // the segment being cut
+  int64_t a_ = 0;         // next shard element to emit
+  bool in_pad_ = false;   // past the segments: the padding overlap
+};
 
 int check_range(const zero_layout_s* h, int64_t begin, int64_t count, const char* who) {
   if (begin < 0 || count < 0 || begin > h->info.shard || count > h->info.shard - begin)
@@ -998,6 +1073,50 @@ bool aligned(const void* p, uintptr_t n) { return (uintptr_t(p) & (n - 1)) == 0;
 
 }  // namespace
 
+// ======================================================= static scratch
+//
+// zero_pack_grads_sqnorm_noalloc keeps its block partial sums in this array
+// instead of a caller's workspace. Each GPU the library runs on holds its own
+// copy, ZERO_NOALLOC_PARTIALS doubles (2 MiB), until the process ends. In
+// host code `scratch` only names the array: its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+static __device__ __align__(256) double scratch[ZERO_NOALLOC_PARTIALS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<double*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device (looked up on the
+// first call for each device).
+int scratch_address(double** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ZERO_EINVAL, "%s: device %d is beyond the %d devices the library tracks", who, dev, kMaxDevices);
+  double* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || addr == nullptr)
+        return fail(ZERO_EHIP, "%s: hipGetSymbolAddress of the static scratch on device %d: %s", who, dev,
+                    hipGetErrorString(e));
+      p = static_cast<double*>(addr);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ZERO_OK;
+}
+
+}  // namespace
+
 // ================================================================== C ABI
 
 extern "C" int zero_pack_grads(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
@@ -1055,6 +1174,50 @@ extern "C" int zero_pack_grads_sqnorm(zero_layout_t h, const uint16_t* const* te
   int64_t n_part = 0;
   if (int rc = launch_pieces(pieces, stream, who, part, &n_part)) return rc;
   hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, part, n_part, d_out,
+                     accumulate ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_pack_grads_sqnorm_noalloc(zero_layout_t h, const uint16_t* const* tensor_grads,
+                                              uint16_t* grad_shard, int64_t begin, int64_t count, double* d_out,
+                                              int32_t accumulate, hipStream_t stream) {
+  static const char* who = "zero_pack_grads_sqnorm_noalloc";
+  if (h == nullptr || tensor_grads == nullptr || grad_shard == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL handle, tensor array or shard", who);
+  if (d_out == nullptr) return fail(ZERO_EINVAL, "%s: NULL output", who);
+  if (int rc = check_range(h, begin, count, who)) return rc;
+  if (uintptr_t(grad_shard) & 1u) return fail(ZERO_EINVAL, "%s: shard pointer is not 2-byte aligned", who);
+  uint16_t* const* grads = const_cast<uint16_t* const*>(tensor_grads);
+  // pass 1: check the tensor pointers and bound the partial sums, as
+  // zero_pack_sqnorm_workspace_bytes does
+  Piece batch[kCopyMaxPieces];
+  int64_t bound = 0;
+  {
+    PieceCursor cur(h, grads, grad_shard, begin, count, true);
+    for (int64_t n; (n = cur.next(batch, kCopyMaxPieces, who)) != 0;) {
+      if (n < 0) return int(n);
+      for (int64_t i = 0; i < n; ++i) bound += (batch[i].len + kCopySqElemPerBlock - 1) / kCopySqElemPerBlock + 1;
+    }
+  }
+  if (bound > ZERO_NOALLOC_PARTIALS)
+    return fail(ZERO_EINVAL,
+                "%s: the range [%lld, +%lld) needs up to %lld partial sums; the static scratch holds %d "
+                "(split the range, or use zero_pack_grads_sqnorm with a workspace)",
+                who, (long long)begin, (long long)count, (long long)bound, ZERO_NOALLOC_PARTIALS);
+  double* part = nullptr;
+  if (int rc = scratch_address(&part, who)) return rc;
+  // pass 2: the launches, each block writing its partial sum to the next slot
+  int64_t done = 0;
+  PieceCursor cur(h, grads, grad_shard, begin, count, true);
+  for (int64_t n; (n = cur.next(batch, kCopyMaxPieces, who)) != 0;) {
+    if (n < 0) return int(n);
+    int64_t n_part = 0;
+    if (int rc = launch_pieces(batch, size_t(n), stream, who, part + done, &n_part)) return rc;
+    done += n_part;
+  }
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kSqFinalThreads), 0, stream, part, done, d_out,
                      accumulate ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));

@@ -22,6 +22,7 @@ ZERO_ENOMEM = -4
 ZERO_STATE_TILE = 8192      # elements per tile of the fp32 state buffer (include/zero.h)
 ZERO_PIECES_PER_LAUNCH = 64            # tensor pieces one launch carries (include/zero.h)
 ZERO_ADAMW_LAUNCH_ELEMS = 1 << 27      # longer update ranges take several launches
+ZERO_NOALLOC_PARTIALS = 1 << 18        # partial sums the static scratch of the no-allocation call holds
 
 
 class ZeroError(RuntimeError):
@@ -77,6 +78,7 @@ _SIGNATURES = {
     "zero_pack_sqnorm_workspace_bytes": (ctypes.c_size_t, [_VP, _I64, _I64]),
     "zero_pack_grads_sqnorm": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP, _I32, _VP,
                                               ctypes.c_size_t, _VP]),
+    "zero_pack_grads_sqnorm_noalloc": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP, _I32, _VP]),
     "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_sum_partials": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
     "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
@@ -278,6 +280,16 @@ def zero_pack_grads_sqnorm(layout: Layout, tensor_grads, grad_shard, begin: int,
     _check("zero_pack_grads_sqnorm", library().zero_pack_grads_sqnorm(
         layout.handle, arr, _ptr(grad_shard), begin, count, _ptr(out), 1 if accumulate else 0,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def zero_pack_grads_sqnorm_noalloc(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, out,
+                                   accumulate: bool, stream=None):
+    arr = _tensor_array(layout, tensor_grads)
+    if count > 0:
+        _need(grad_shard, 2 * (begin + count), "gradient shard")
+    _need(out, 8, "output")
+    _check("zero_pack_grads_sqnorm_noalloc", library().zero_pack_grads_sqnorm_noalloc(
+        layout.handle, arr, _ptr(grad_shard), begin, count, _ptr(out), 1 if accumulate else 0, _stream(stream)))
 
 
 def zero_unpack_params(layout: Layout, param_shard, tensor_params, begin: int, count: int, stream=None):

@@ -175,6 +175,32 @@ int zero_pack_grads_sqnorm(zero_layout_t h, const uint16_t* const* tensor_grads,
                            void* d_workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * zero_pack_grads_sqnorm_noalloc -- zero_pack_grads_sqnorm without a
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The block partial sums go to a static device array that the library holds
+ * on every GPU it runs on: ZERO_NOALLOC_PARTIALS doubles (2 MiB) per GPU,
+ * kept until the process ends. The call allocates nothing (device or host)
+ * and uses the same kernels in the same order as zero_pack_grads_sqnorm, so
+ * its results are bit-identical to that call's.
+ * Arguments, results and errors as zero_pack_grads_sqnorm, without the
+ * workspace. Limit: the range may need at most ZERO_NOALLOC_PARTIALS partial
+ * sums, i.e. zero_pack_sqnorm_workspace_bytes(h, begin, count) <=
+ * 8 * ZERO_NOALLOC_PARTIALS (a range in one piece of up to 2,147,475,456
+ * elements); a larger range is refused with ZERO_EINVAL before anything is
+ * enqueued. Every call on a GPU shares that GPU's array and overwrites what
+ * the previous call left (each call writes every partial it reads, so nothing
+ * needs clearing): calls whose execution overlaps on one GPU (on different
+ * streams, or from different host threads without ordering) race and give
+ * wrong sums. ZERO_EHIP also reports a failed hipGetDevice or
+ * hipGetSymbolAddress (the array's address on the current device, looked up
+ * on the first call for each device). */
+#define ZERO_NOALLOC_PARTIALS (1 << 18)
+int zero_pack_grads_sqnorm_noalloc(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                                   int64_t begin, int64_t count, double* d_out, int32_t accumulate,
+                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * zero_shard_sqnorm -- the rank's part of the global gradient norm.
  * *d_out = sum of g*g over the count bf16 values at d_grad (or *d_out += that
  * sum when accumulate != 0), each square exact in fp64 and the sum carried in

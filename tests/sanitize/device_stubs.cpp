@@ -7,6 +7,7 @@ extern "C" {
 int zero_pack_grads(zero_layout_t, const uint16_t* const*, uint16_t*, int64_t, int64_t, hipStream_t) { return -1; }
 size_t zero_pack_sqnorm_workspace_bytes(zero_layout_t, int64_t, int64_t) { return 0; }
 int zero_pack_grads_sqnorm(zero_layout_t, const uint16_t* const*, uint16_t*, int64_t, int64_t, double*, int32_t, void*, size_t, hipStream_t) { return -1; }
+int zero_pack_grads_sqnorm_noalloc(zero_layout_t, const uint16_t* const*, uint16_t*, int64_t, int64_t, double*, int32_t, hipStream_t) { return -1; }
 size_t zero_sqnorm_workspace_bytes(int64_t) { return 0; }
 int zero_shard_sqnorm(const uint16_t*, int64_t, double*, int32_t, void*, size_t, hipStream_t) { return -1; }
 int zero_sum_partials(const double*, int64_t, double*, int32_t, hipStream_t) { return -1; }
