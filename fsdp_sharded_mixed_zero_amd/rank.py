@@ -139,17 +139,45 @@ class RankShard:
         for i in self.touched:
             synth.device_grad_(self.grads[i], self.wl, step, salt=i)
 
-    def other_rank_real(self, r):
-        """Parameters (not padding) rank r owns."""
-        S, psi = self.shard, self.info["psi"]
-        return max(0, min(S, psi - r * S))
+    def fill_other_ranks(self, step=None):
+        """The other ranks' partial sums of squares, each from its own slice of
+        the model's gradients: every tensor that reaches another rank's shard
+        is drawn on the device exactly as this rank draws its own tensors
+        (synth.device_grad_, stream pieces by tensor index, gradients of
+        ``step``, by default the workload's), and the sum of squares of each
+        other rank's part of it is added into that rank's slot with
+        zero_shard_sqnorm, in tensor order. Padding adds nothing. This rank's
+        slot is left at 0 (the step computes it). The slots stand for what the
+        all-reduce of the ranks' partial sums would deliver ("ZeRO-3 核心流程",
+        pitfall 1: the clip norm covers every rank's slice). Set-up work, not
+        part of a step: it draws the whole model's gradients once."""
+        wl, S = self.wl, self.shard
+        step = wl.step if step is None else step
+        self.rank_sq.zero_()
+        work = [(i, n, off) for i, (n, off) in enumerate(zip(wl.sizes, self._flat_offsets())) if n > 0
+                and not (off // S == self.rank and (off + n - 1) // S == self.rank)]
+        if not work:
+            torch.cuda.synchronize(self.device)
+            return
+        longest = max(n for _, n, _ in work)
+        buf = torch.empty(longest, dtype=torch.bfloat16, device=self.device)
+        ws = torch.empty((zero.zero_sqnorm_workspace_bytes(longest) + 7) // 8, dtype=torch.float64,
+                         device=self.device)
+        for i, n, off in work:
+            g = synth.device_grad_(buf[:n], wl, step, salt=i)
+            for r in range(off // S, (off + n - 1) // S + 1):
+                if r == self.rank:
+                    continue
+                a, b = max(off, r * S) - off, min(off + n, (r + 1) * S) - off
+                zero.zero_shard_sqnorm(g[a:], b - a, self.rank_sq[r:r + 1], True, ws)
+        torch.cuda.synchronize(self.device)
 
-    def fill_other_ranks(self):
-        """The other ranks' partial sums of squares: their expected value under
-        the gradient distribution (this rank's entry is computed each step)."""
-        vals = [self.other_rank_real(r) * self.wl.grad_sq_mean() for r in range(self.wl.n_d)]
-        vals[self.rank] = 0.0
-        self.rank_sq.copy_(torch.tensor(vals, dtype=torch.float64))
+    def _flat_offsets(self):
+        out, off = [], 0
+        for n in self.wl.sizes:
+            out.append(off)
+            off += n
+        return out
 
     # --------------------------------------------------------------- step
     def hparams(self, step):

@@ -99,8 +99,9 @@ class Workload:
     notes: dict = field(default_factory=dict, compare=False)
 
     def grad_sq_mean(self):
-        """Expected square of one gradient entry (used for the other ranks'
-        partial sums, which a single GPU cannot compute)."""
+        """Expected square of one gradient entry (the benchmark's CPU baseline
+        takes the other ranks' share of the norm of its timing sample from
+        it)."""
         s2 = self.grad_std ** 2
         return (1 - self.spike_frac) * s2 + self.spike_frac * s2 * self.spike_scale ** 2
 

@@ -1,8 +1,13 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times (RankShard.step: whole shard, or 5e7-element buckets for the
-70B shard). The oracle checks sampled ranges element by element; the rank's
-whole-shard sum of squares is recomputed by the oracle over the full shard,
-packed by the oracle from the per-tensor gradients.
+70B shard). The oracle checks element by element a window across every
+tensor seam in the shard, every bucket seam and every seam between update
+launches, plus random ranges (every element of the GPT-2 and 7.5B shards is
+checked in test_gpu_whole_shard.py); the rank's whole-shard sum of squares is
+recomputed by the oracle over the full shard, packed by the oracle from the
+per-tensor gradients. The other ranks' partial sums come from the model's
+generated gradients: the library's (RankShard.fill_other_ranks) are checked
+against torch's, and the oracle's global norm takes torch's.
 
 Per workload:
   * pack: sampled shard ranges equal the oracle's pack of the same ranges of
@@ -48,18 +53,60 @@ class DeviceTensor:
         return u16(self.t[sl])
 
 
-def sample_ranges(lay, wl, rng):
+SEAM = 4096                # elements of a window across a seam
+
+
+def update_launch_seams(S, bucket):
+    """Where the update's launches meet inside a call (ranges longer than
+    ZERO_ADAMW_LAUNCH_ELEMS are cut into equal launches of whole state
+    tiles)."""
+    out = []
+    for b0 in (range(0, S, bucket) if bucket else [0]):
+        n = min(bucket, S - b0) if bucket else S
+        k = -(-n // zero.ZERO_ADAMW_LAUNCH_ELEMS)
+        chunk = -(-(-(-n // k)) // zero.ZERO_STATE_TILE) * zero.ZERO_STATE_TILE
+        out += [b0 + j for j in range(chunk, n, chunk)]
+    return out
+
+
+def sample_ranges(lay, wl, rng, bucket=None):
+    """Random windows of SAMPLE elements, the shard's ends, and a SEAM-element
+    window (at an odd offset) across every tensor seam, bucket seam and
+    update-launch seam."""
     S = lay.shard
+    bucket = wl.bucket if bucket is None else bucket
     c = min(SAMPLE, S)
-    starts = {0, S - c}
-    for seg in lay.segments[1:6]:                 # tensor boundaries inside the shard
-        starts.add(min(max(0, seg.dst_off - c // 2), S - c))
-    if wl.bucket:
-        for b in range(wl.bucket, S, wl.bucket * 37):
-            starts.add(min(max(0, b - c // 2 - 3), S - c))    # odd offsets across buckets
+    wins = {(0, c), (S - c, c)}
     for _ in range(4):
-        starts.add(int(rng.integers(0, S - c + 1)))
-    return sorted((s, c) for s in starts)
+        wins.add((int(rng.integers(0, S - c + 1)), c))
+    w = min(SEAM, S)
+    seams = [seg.dst_off for seg in lay.segments[1:]]
+    if bucket:
+        seams += list(range(bucket, S, bucket))
+    seams += update_launch_seams(S, bucket)
+    for x in seams:
+        wins.add((min(max(0, x - w // 2 - 3), S - w), w))
+    # merge overlapping windows (a range is compared as one piece)
+    out = []
+    for b, n in sorted(wins):
+        if out and b <= out[-1][0] + out[-1][1]:
+            lo = out[-1][0]
+            out[-1] = (lo, max(out[-1][0] + out[-1][1], b + n) - lo)
+        else:
+            out.append((b, n))
+    return out
+
+
+_TORCH_OTHERS = {}
+
+
+def other_partials(wl, S, rank):
+    """torch's partial sums of the other ranks (computed once per workload)."""
+    from other_ranks import torch_rank_partials
+    key = (wl.name, rank, wl.step)
+    if key not in _TORCH_OTHERS:
+        _TORCH_OTHERS[key] = torch_rank_partials(wl, S, wl.step, rank)
+    return _TORCH_OTHERS[key]
 
 
 def oracle_partial(lay, tensors, S):
@@ -125,7 +172,9 @@ def test_workload_full_size(name, fused_norm, bucket, fused_unpack):
     rs.fill_state(on_chunk=capture)
     rs.fill_grads(wl.step)
     rs.fill_other_ranks()
-    others = rs.rank_sq.cpu().numpy().copy()
+    from other_ranks import check_library_partials
+    others = other_partials(wl, S, rs.rank)
+    check_library_partials(rs.rank_sq.cpu().numpy(), others, rs.rank)
     lazy = [None if t is None else DeviceTensor(t) for t in rs.grads]
     grads_before = {b: O.pack(lay, lazy, b, c) for b, c in ranges}
     torch.cuda.synchronize()
@@ -220,7 +269,9 @@ def test_workload_grad_accumulation(name, micro):
 
     rs.fill_state(on_chunk=capture)
     rs.fill_other_ranks()
-    others = rs.rank_sq.cpu().numpy().copy()
+    from other_ranks import check_library_partials
+    others = other_partials(wl, S, rs.rank)
+    check_library_partials(rs.rank_sq.cpu().numpy(), others, rs.rank)
     lazy = [None if t is None else DeviceTensor(t) for t in rs.grads]
     o_acc = [None]
 
