@@ -130,11 +130,12 @@ def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unp
 
 def steps_traced(counts, wl, S, combine=False):
     """Steps a trace covers (warm-up included): the sum-of-squares final
-    kernel runs once per bucket in every mode (plus once for the combine of a
-    bucketed default step), whereas an update over more than 64 tensor pieces
-    takes several launches."""
+    kernel runs once per bucket in the modes without the combine, and once
+    per step (the combine) in a bucketed default step, whose buckets' own
+    final stages run as one row-sum launch; an update over more than 64 tensor
+    pieces takes several launches."""
     pieces = -(-S // wl.bucket) if wl.bucket > 0 else 1
-    return counts["sqnorm_final_kernel"] / (pieces + (1 if combine and pieces > 1 else 0))
+    return counts["sqnorm_final_kernel"] / (1 if combine else pieces)
 
 
 def code_text(text):
@@ -213,7 +214,7 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
     f_write = known_kib / write[copy]
     kernels = {}
     for k in fetch:
-        if k not in per_dispatch and not k.startswith("sqnorm_final"):
+        if k not in per_dispatch and not k.startswith(("sqnorm_final", "sum_rows")):
             continue
         bytes_ = (fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024.0
         kernels[k] = {"fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
@@ -287,7 +288,7 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
              "GB/s at avg | % of 8 TB/s | busy us/step | GB/s (busy) | % (busy) |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for short, row in rows.items():
-        if short not in algo and not short.startswith("sqnorm_final"):
+        if short not in algo and not short.startswith(("sqnorm_final", "sum_rows")):
             continue
         calls = int(row["Calls"])
         per_step = calls / steps_run

@@ -13,8 +13,9 @@
 //
 //   copy_pieces_kernel<SQ>    pack (tensors -> shard) and unpack (shard ->
 //                             tensors); with SQ the pack also sums squares
-//   sqnorm_partial_kernel, sqnorm_f32_partial_kernel, sqnorm_final_kernel
-//                             deterministic two-stage sum of squares (fp64)
+//   sqnorm_partial_kernel, sqnorm_f32_partial_kernel, sqnorm_final_kernel,
+//   sum_rows_kernel           deterministic two-stage sum of squares (fp64);
+//                             rows: the final stage of many buckets at once
 //   adamw_vec_kernel, adamw_elem_kernel
 //                             clip + AdamW + bf16 cast, 28 bytes per element
 //   adamw_unpack_vec_kernel, adamw_unpack_elem_kernel
@@ -519,9 +520,10 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_f32_partial_kernel(const fl
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const double* __restrict__ partial,
-                                                                        int64_t n, double* __restrict__ out,
-                                                                        int accumulate) {
+// The fixed-order sum of n doubles by one block of kSqFinalThreads threads;
+// every thread calls it, thread 0 writes *out (or adds to it).
+__device__ __forceinline__ void final_sum(const double* __restrict__ partial, int64_t n, double* __restrict__ out,
+                                          int accumulate) {
   // The partials were just written by blocks on every XCD, so each load is a
   // trip to memory: sixteen independent loads per lane per round keep the
   // rounds few (a 1.7 G-element shard has ~2e5 partials). The accumulators
@@ -548,6 +550,29 @@ __global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const dou
   }
   const double s = block_sum<kSqFinalThreads>(acc[0]);
   if (threadIdx.x == 0) *out = accumulate ? *out + s : s;
+}
+
+__global__ __launch_bounds__(kSqFinalThreads) void sqnorm_final_kernel(const double* __restrict__ partial,
+                                                                        int64_t n, double* __restrict__ out,
+                                                                        int accumulate) {
+  final_sum(partial, n, out, accumulate);
+}
+
+// Rows of partial sums, one block each: out[r] (+)= the sum of row r, in the
+// order sqnorm_final_kernel adds the same values.
+constexpr int kMaxRowsPerLaunch = 192;
+
+struct Rows {
+  int32_t n;
+  int64_t begin[kMaxRowsPerLaunch];
+  int64_t len[kMaxRowsPerLaunch];
+};
+static_assert(sizeof(Rows) + 3 * sizeof(void*) <= 4096, "kernel arguments fit the 4 KiB segment");
+
+__global__ __launch_bounds__(kSqFinalThreads) void sum_rows_kernel(const double* __restrict__ partial, const Rows R,
+                                                                    double* __restrict__ out, int accumulate) {
+  const int r = blockIdx.x;
+  final_sum(partial + R.begin[r], R.len[r], out + r, accumulate);
 }
 
 // ============================================================ fused AdamW
@@ -1278,6 +1303,57 @@ extern "C" int zero_sum_partials(const double* d_partials, int64_t n, double* d_
                      accumulate ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return zero::ok();
+}
+
+extern "C" int zero_pack_grads_sqnorm_partials(zero_layout_t h, const uint16_t* const* tensor_grads,
+                                               uint16_t* grad_shard, int64_t begin, int64_t count,
+                                               double* d_partials, size_t cap_bytes, int64_t* n_partials,
+                                               hipStream_t stream) {
+  static const char* who = "zero_pack_grads_sqnorm_partials";
+  if (h == nullptr || tensor_grads == nullptr || grad_shard == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL handle, tensor array or shard", who);
+  if (d_partials == nullptr || n_partials == nullptr) return fail(ZERO_EINVAL, "%s: NULL partials or count", who);
+  if (int rc = check_range(h, begin, count, who)) return rc;
+  if (uintptr_t(grad_shard) & 1u) return fail(ZERO_EINVAL, "%s: shard pointer is not 2-byte aligned", who);
+  if (uintptr_t(d_partials) & 7u) return fail(ZERO_EINVAL, "%s: partials are not 8-byte aligned", who);
+  const int64_t bound = std::max<int64_t>(pieces_block_bound(pack_piece_lengths(h, begin, count)), 1);
+  if (cap_bytes < size_t(bound) * sizeof(double))
+    return fail(ZERO_EINVAL, "%s: room for %zu bytes of partial sums, need %zu", who, cap_bytes,
+                size_t(bound) * sizeof(double));
+  std::vector<Piece> pieces;
+  if (int rc = build_pieces(h, const_cast<uint16_t* const*>(tensor_grads), grad_shard, begin, count, true,
+                            &pieces, who))
+    return rc;
+  int64_t n = 0;
+  if (int rc = launch_pieces(pieces, stream, who, d_partials, &n)) return rc;
+  *n_partials = n;
+  return zero::ok();
+}
+
+extern "C" int zero_sum_partials_rows(const double* d_partials, const int64_t* row_begin, const int64_t* row_len,
+                                      int64_t n_rows, double* d_out, int32_t accumulate, hipStream_t stream) {
+  static const char* who = "zero_sum_partials_rows";
+  if (n_rows < 0) return fail(ZERO_EINVAL, "%s: n_rows < 0", who);
+  if (n_rows == 0) return zero::ok();
+  if (d_partials == nullptr || row_begin == nullptr || row_len == nullptr || d_out == nullptr)
+    return fail(ZERO_EINVAL, "%s: NULL argument", who);
+  if ((uintptr_t(d_partials) | uintptr_t(d_out)) & 7u) return fail(ZERO_EINVAL, "%s: misaligned pointer", who);
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (row_begin[r] < 0 || row_len[r] < 0)
+      return fail(ZERO_EINVAL, "%s: row %lld has a negative start or length", who, (long long)r);
+  for (int64_t r0 = 0; r0 < n_rows; r0 += kMaxRowsPerLaunch) {
+    Rows R{};
+    R.n = int32_t(std::min<int64_t>(kMaxRowsPerLaunch, n_rows - r0));
+    for (int32_t i = 0; i < R.n; ++i) {
+      R.begin[i] = row_begin[r0 + i];
+      R.len[i] = row_len[r0 + i];
+    }
+    hipLaunchKernelGGL(sum_rows_kernel, dim3(unsigned(R.n)), dim3(kSqFinalThreads), 0, stream, d_partials, R,
+                       d_out + r0, accumulate ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  }
   return zero::ok();
 }
 

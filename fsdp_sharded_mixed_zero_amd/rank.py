@@ -98,8 +98,13 @@ class RankShard:
         n_pieces = len(self.pieces())
         self.bucketed = n_pieces > 1 and not flat and accum_steps == 1 and fused_norm
         self.bucket_sq = torch.zeros(n_pieces, dtype=torch.float64, device=dev) if n_pieces > 1 else None
+        if self.bucketed:
+            # each bucket's block partial sums in its own slice of one buffer
+            caps = [zero.zero_pack_sqnorm_workspace_bytes(self.layout, b, n) // 8 for b, n in self.pieces()]
+            self.part_off = [sum(caps[:k]) for k in range(n_pieces)]
+            self.part_cap = caps
+            self.bucket_partials = torch.empty(sum(caps), dtype=torch.float64, device=dev)
         self.n_streams = max(1, int(streams)) if self.bucketed else 1
-        self.workspaces = [self.workspace] + [torch.empty_like(self.workspace) for _ in range(self.n_streams - 1)]
         self.streams = [torch.cuda.Stream(device=dev) for _ in range(self.n_streams)] if self.n_streams > 1 else []
         if fill:
             self.fill_state()
@@ -252,22 +257,28 @@ class RankShard:
             mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
 
-    def pack_norm_buckets(self, own, stream, pieces=None):
-        """Pack + sum of squares of every bucket, each bucket's sum in its own
-        slot, on the step's streams in turn; then, on ``stream`` once all are
-        done, ``own`` = the slots added in a fixed order. The result does not
-        depend on the number of streams."""
-        pieces = self.pieces() if pieces is None else pieces
+    def pack_norm_buckets(self, own, stream):
+        """Pack + sum of squares of every bucket on the step's streams in turn,
+        each bucket's block partial sums in its own slice of bucket_partials;
+        then, on ``stream`` once all are done, one launch reduces every slice
+        into the bucket's slot (zero_sum_partials_rows) and ``own`` = the slots
+        added in a fixed order. Each bucket's sum is the one
+        zero_pack_grads_sqnorm would give, and the result does not depend on
+        the number of streams."""
+        pieces = self.pieces()
         main = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
         for st in self.streams:
             st.wait_stream(main)
+        counts = []
         for k, (b, n) in enumerate(pieces):
-            i = k % self.n_streams
-            st = self.streams[i].cuda_stream if self.streams else main.cuda_stream
-            zero.zero_pack_grads_sqnorm(self.layout, self.grad_ptrs, self.grad_shard, b, n, self.bucket_sq[k:k + 1],
-                                        False, self.workspaces[i], stream=st)
+            st = self.streams[k % self.n_streams].cuda_stream if self.streams else main.cuda_stream
+            counts.append(zero.zero_pack_grads_sqnorm_partials(
+                self.layout, self.grad_ptrs, self.grad_shard, b, n, self.bucket_partials[self.part_off[k]:],
+                8 * self.part_cap[k], stream=st))
         for st in self.streams:
             main.wait_stream(st)
+        zero.zero_sum_partials_rows(self.bucket_partials, self.part_off, counts, self.bucket_sq, False,
+                                    stream=main.cuda_stream)
         zero.zero_sum_partials(self.bucket_sq, len(pieces), own, False, stream=main.cuda_stream)
 
     def _step_buckets(self, hp, own, pieces, stream, timing, events, phases):
@@ -297,7 +308,7 @@ class RankShard:
             for st in self.streams:
                 main.wait_stream(st)
 
-        timed("pack_sqnorm", lambda: self.pack_norm_buckets(own, main, pieces))
+        timed("pack_sqnorm", lambda: self.pack_norm_buckets(own, main))
         if self.fused_unpack:
             timed("adamw", lambda: on_streams(lambda b, n, st: zero.zero_adamw_step_unpack(
                 self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq, self.wl.n_d,

@@ -81,6 +81,10 @@ _SIGNATURES = {
     "zero_pack_grads_sqnorm_noalloc": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP, _I32, _VP]),
     "zero_shard_sqnorm": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "zero_sum_partials": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
+    "zero_pack_grads_sqnorm_partials": (ctypes.c_int, [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, _VP,
+                                                       ctypes.c_size_t, ctypes.POINTER(_I64), _VP]),
+    "zero_sum_partials_rows": (ctypes.c_int, [_VP, ctypes.POINTER(_I64), ctypes.POINTER(_I64), _I64, _VP, _I32,
+                                              _VP]),
     "zero_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                        ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
     "zero_adamw_step_f32grad": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
@@ -322,6 +326,34 @@ def zero_sum_partials(partials, n: int, out, accumulate: bool = False, stream=No
     _need(out, 8, "output")
     _check("zero_sum_partials", library().zero_sum_partials(
         _ptr(partials), n, _ptr(out), 1 if accumulate else 0, _stream(stream)))
+
+
+def zero_pack_grads_sqnorm_partials(layout: Layout, tensor_grads, grad_shard, begin: int, count: int, partials,
+                                    cap_bytes: int | None = None, stream=None) -> int:
+    """Returns the number of partial sums written."""
+    arr = _tensor_array(layout, tensor_grads)
+    if count > 0:
+        _need(grad_shard, 2 * (begin + count), "gradient shard")
+    if cap_bytes is None:
+        cap_bytes = partials.numel() * partials.element_size()
+    n = ctypes.c_int64(0)
+    _check("zero_pack_grads_sqnorm_partials", library().zero_pack_grads_sqnorm_partials(
+        layout.handle, arr, _ptr(grad_shard), begin, count, _ptr(partials), cap_bytes, ctypes.byref(n),
+        _stream(stream)))
+    return int(n.value)
+
+
+def zero_sum_partials_rows(partials, row_begin, row_len, out, accumulate: bool = False, stream=None):
+    n = len(row_begin)
+    if len(row_len) != n:
+        raise ValueError("row_begin and row_len differ in length")
+    if n > 0:
+        _need(partials, 8 * max(b + c for b, c in zip(row_begin, row_len)), "partial sums")
+        _need(out, 8 * n, "output")
+    begins = (ctypes.c_int64 * n)(*row_begin)
+    lens = (ctypes.c_int64 * n)(*row_len)
+    _check("zero_sum_partials_rows", library().zero_sum_partials_rows(
+        _ptr(partials), begins, lens, n, _ptr(out), 1 if accumulate else 0, _stream(stream)))
 
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0,

@@ -237,6 +237,42 @@ int zero_shard_sqnorm(const uint16_t* d_grad, int64_t count, double* d_out, int3
 int zero_sum_partials(const double* d_partials, int64_t n, double* d_out, int32_t accumulate, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * zero_pack_grads_sqnorm_partials, zero_sum_partials_rows -- the bucketed
+ * form of zero_pack_grads_sqnorm, with one final stage for all buckets. A
+ * shard processed in constant-size buckets (notes on the ZeRO paper, section
+ * 5.2, constant buffer size; "ZeRO-3 核心流程", the prefetch bucket) packs
+ * each bucket on any stream, leaving its block partial sums in its own slice
+ * of one buffer; once every bucket is done, one launch reduces each slice, and
+ * zero_sum_partials combines the buckets' sums.
+ *
+ * zero_pack_grads_sqnorm_partials packs [begin, begin+count) exactly as
+ * zero_pack_grads does and writes the sum of squares of each of its blocks to
+ * d_partials[0 .. *n_partials) (device, 8-byte aligned; *n_partials is a HOST
+ * int64, set before the call returns). cap_bytes, the room at d_partials, must
+ * be at least zero_pack_sqnorm_workspace_bytes(h, begin, count); the count
+ * depends on the layout, the range and the pointers' alignment only.
+ * zero_pack_grads_sqnorm over the same range computes the same partials and
+ * adds them as zero_sum_partials_rows does a row of that length, so the
+ * results are bit-identical.
+ * Errors: as zero_pack_grads_sqnorm, with cap_bytes for the workspace size
+ * and ZERO_EINVAL for a NULL n_partials.
+ *
+ * zero_sum_partials_rows: for r in [0, n_rows), d_out[r] = the sum of the
+ * row_len[r] doubles at d_partials + row_begin[r] (or d_out[r] += it when
+ * accumulate != 0), each row in the order zero_sum_partials adds that many
+ * values (bit-identical to it). row_begin, row_len: HOST arrays of n_rows
+ * int64 (element offsets and counts, >= 0); d_out: device array of n_rows
+ * doubles, not overlapping the rows. One launch per 192 rows.
+ * Errors: ZERO_EINVAL for n_rows < 0, NULL arguments (allowed when n_rows ==
+ * 0), pointers not 8-byte aligned or a negative start or length; ZERO_EHIP if
+ * a launch fails. */
+int zero_pack_grads_sqnorm_partials(zero_layout_t h, const uint16_t* const* tensor_grads, uint16_t* grad_shard,
+                                    int64_t begin, int64_t count, double* d_partials, size_t cap_bytes,
+                                    int64_t* n_partials, hipStream_t stream);
+int zero_sum_partials_rows(const double* d_partials, const int64_t* row_begin, const int64_t* row_len,
+                           int64_t n_rows, double* d_out, int32_t accumulate, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Layout of the fp32 optimizer state (12 bytes per element: master, m, v).
  * The state of an n-element shard is ONE buffer of 3*n floats in tiles of
  * ZERO_STATE_TILE elements. Tile k covers elements [k*T, k*T + L_k) with

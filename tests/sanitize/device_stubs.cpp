@@ -11,6 +11,8 @@ int zero_pack_grads_sqnorm_noalloc(zero_layout_t, const uint16_t* const*, uint16
 size_t zero_sqnorm_workspace_bytes(int64_t) { return 0; }
 int zero_shard_sqnorm(const uint16_t*, int64_t, double*, int32_t, void*, size_t, hipStream_t) { return -1; }
 int zero_sum_partials(const double*, int64_t, double*, int32_t, hipStream_t) { return -1; }
+int zero_pack_grads_sqnorm_partials(zero_layout_t, const uint16_t* const*, uint16_t*, int64_t, int64_t, double*, size_t, int64_t*, hipStream_t) { return -1; }
+int zero_sum_partials_rows(const double*, const int64_t*, const int64_t*, int64_t, double*, int32_t, hipStream_t) { return -1; }
 int zero_adamw_step(const uint16_t*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, hipStream_t) { return -1; }
 int zero_state_import(const float*, const float*, const float*, float*, int64_t, hipStream_t) { return -1; }
 int zero_state_export(const float*, float*, float*, float*, int64_t, hipStream_t) { return -1; }

@@ -79,3 +79,62 @@ def test_step_on_a_given_stream_times_its_own_launches():
             assert e0.elapsed_time(e1) * 1e3 > (50.0 if phase == "adamw" else 5.0), (phase, e0.elapsed_time(e1))
         for buf in ("state", "param_shard", "grad_shard", "rank_sq"):
             assert torch.equal(bits(getattr(side, buf)), bits(getattr(ref, buf))), (k, buf)
+
+
+def test_bucket_sums_equal_the_per_bucket_call():
+    """The bucketed step's sums of squares (each bucket's block partials in its
+    own slice, one row-sum launch) equal, bit for bit, zero_pack_grads_sqnorm
+    called bucket by bucket; the packed shard is the same too."""
+    from fsdp_sharded_mixed_zero_amd import zero
+
+    wl = synth.WORKLOADS["gpt2-1.5b"]
+    rs = RankShard(wl, bucket=3_000_017, streams=2)
+    assert rs.bucketed
+    own = torch.zeros(1, dtype=torch.float64, device="cuda")
+    rs.pack_norm_buckets(own, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    shard = rs.grad_shard.clone()
+    per_call = torch.zeros(len(rs.pieces()), dtype=torch.float64, device="cuda")
+    for k, (b, n) in enumerate(rs.pieces()):
+        zero.zero_pack_grads_sqnorm(rs.layout, rs.grad_ptrs, rs.grad_shard, b, n, per_call[k:k + 1], False,
+                                    rs.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(per_call), bits(rs.bucket_sq))
+    assert torch.equal(bits(shard), bits(rs.grad_shard))
+    again = torch.zeros(1, dtype=torch.float64, device="cuda")
+    zero.zero_sum_partials(per_call, len(rs.pieces()), again)
+    assert torch.equal(bits(again), bits(own))
+
+
+def test_partial_rows_equal_sum_partials():
+    """zero_sum_partials_rows over 400 rows of random lengths (0 to 20000,
+    three launches of at most 192 rows) equals zero_sum_partials on each row
+    bit for bit, plain and accumulating; and the calls refuse what they
+    should."""
+    from fsdp_sharded_mixed_zero_amd import zero
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    lens = torch.randint(0, 20001, (400,), generator=g, device="cuda").tolist()
+    lens[3] = 0
+    begins = [sum(lens[:r]) + 7 * r for r in range(400)]             # gaps between the rows
+    data = torch.randn(begins[-1] + lens[-1] + 5, dtype=torch.float64, device="cuda", generator=g) ** 2
+    out = torch.full((400,), 0.5, dtype=torch.float64, device="cuda")
+    zero.zero_sum_partials_rows(data, begins, lens, out, accumulate=False)
+    acc = torch.full((400,), 0.5, dtype=torch.float64, device="cuda")
+    zero.zero_sum_partials_rows(data, begins, lens, acc, accumulate=True)
+    want = torch.zeros(400, dtype=torch.float64, device="cuda")
+    want_acc = torch.full((400,), 0.5, dtype=torch.float64, device="cuda")
+    for r in range(400):
+        zero.zero_sum_partials(data[begins[r]:], lens[r], want[r:r + 1])
+        zero.zero_sum_partials(data[begins[r]:], lens[r], want_acc[r:r + 1], accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(want))
+    assert torch.equal(bits(acc), bits(want_acc))
+    assert float(out[3]) == 0.0
+    with pytest.raises(zero.ZeroError):
+        zero.zero_sum_partials_rows(data, [0, -1], [1, 1], out)
+    lay = zero.zero_layout([1000], 1, 0, 1)
+    grad = torch.zeros(1000, dtype=torch.bfloat16, device="cuda")
+    shard = torch.empty_like(grad)
+    with pytest.raises(zero.ZeroError, match="room for"):
+        zero.zero_pack_grads_sqnorm_partials(lay, [grad], shard, 0, 1000, out, 8)
