@@ -138,6 +138,20 @@ def steps_traced(counts, wl, S, combine=False):
     return counts["sqnorm_final_kernel"] / (1 if combine else pieces)
 
 
+def setup_sqnorm_launches(wl):
+    """Launches of each sum-of-squares kernel the benchmark makes before its
+    first step: RankShard.fill_other_ranks runs one zero_shard_sqnorm (a
+    partial and a final kernel) per part of a tensor in another rank's shard.
+    They come first in a trace, and the summaries leave them out."""
+    from fsdp_sharded_mixed_zero_amd import zero
+    from fsdp_sharded_mixed_zero_amd.rank import other_rank_slices
+    S = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info["shard"]
+    return sum(len(parts) for _, parts in other_rank_slices(wl.sizes, S, wl.rank))
+
+
+SETUP_KERNELS = ("sqnorm_partial_kernel", "sqnorm_final_kernel")
+
+
 def code_text(text):
     """C++ source with its comments removed and blank space collapsed (string
     and character literals kept as written)."""
@@ -185,14 +199,32 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
     import csv
     import glob
 
+    n_setup = setup_sqnorm_launches(wl)
+
     def load(d, counter):
+        """Per kernel, the mean counter value per dispatch (the set-up
+        launches left out) and the dispatch count; the copy kernel's mean is
+        over its largest-grid dispatches only (the copy ceiling's full-size
+        copy)."""
         path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
         per = {}
-        for row in csv.DictReader(open(path)):
+        for i, row in enumerate(csv.DictReader(open(path))):
             if row["Counter_Name"] != counter:
                 continue
-            per.setdefault(kernel_name(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+            per.setdefault(kernel_name(row["Kernel_Name"]), []).append(
+                ((int(row.get("Dispatch_Id") or 0), i), int(row.get("Grid_Size") or 0), float(row["Counter_Value"])))
+        mean, count = {}, {}
+        for k, rows in per.items():
+            rows.sort()                                    # dispatch order
+            if k in SETUP_KERNELS:
+                rows = rows[n_setup:]
+            if k == "copy_pieces_kernel<false>" and not separate_unpack and rows:
+                big = max(g for _, g, _ in rows)
+                rows = [r for r in rows if r[1] == big]
+            if rows:
+                mean[k] = sum(v for _, _, v in rows) / len(rows)
+                count[k] = len(rows)
+        return mean, count
 
     fetch, n_f = load(fetch_dir, "FETCH_SIZE")
     write, n_w = load(write_dir, "WRITE_SIZE")
@@ -200,7 +232,10 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
     S, real, algo = algorithmic_bytes(wl, separate_unpack=separate_unpack)
     steps = steps_traced(n_f, wl, S, combine=True)
     update = update_kernel(separate_unpack=separate_unpack)
-    per_dispatch = {k: algo[k] / (n_f[k] / steps) for k in algo if k in n_f}
+    per_dispatch = {k: algo[k] / (n_f[k] / steps) for k in algo if k in n_f and k != "copy_pieces_kernel<false>"}
+    if separate_unpack:
+        per_dispatch["copy_pieces_kernel<false>"] = algo["copy_pieces_kernel<false>"] / (
+            n_f["copy_pieces_kernel<false>"] / steps)
     copy = "copy_pieces_kernel<false>"
     if separate_unpack:
         known = per_dispatch[copy] / 2               # unpack: as many bytes read as written
@@ -238,23 +273,32 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
 
 
 def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False, separate_unpack=False):
-    """Markdown table of a rocprofv3 kernel-stats CSV of this benchmark, with
-    achieved bandwidth from each kernel's algorithmic bytes per launch (the
-    step's bytes spread over that kernel's launches per step)."""
+    """Markdown table of the launches in a rocprofv3 kernel trace of this
+    benchmark, with achieved bandwidth from each kernel's algorithmic bytes
+    per launch (the step's bytes spread over that kernel's launches per
+    step)."""
     import csv
     import glob
 
-    path = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat, separate_unpack)
-    rows = {kernel_name(r["Name"]): r for r in csv.DictReader(open(path))}
-    # busy time of each kernel: the union of its launches' intervals (launches
-    # on two streams overlap, and each one's duration then includes time the
-    # other stream shares)
+    # every launch from the trace, in time order; the set-up launches of the
+    # sum-of-squares kernels (the other ranks' partial sums) left out
     spans = {}
     for tpath in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
         for r in csv.DictReader(open(tpath)):
             spans.setdefault(kernel_name(r["Kernel_Name"]), []).append(
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    n_setup = setup_sqnorm_launches(wl)
+    for k in spans:
+        spans[k].sort()
+        if k in SETUP_KERNELS:
+            spans[k] = spans[k][n_setup:]
+    rows = {k: {"Calls": len(iv), "AverageNs": sum(b - a for a, b in iv) / len(iv),
+                "MinNs": min(b - a for a, b in iv), "MaxNs": max(b - a for a, b in iv)}
+            for k, iv in spans.items() if iv}
+    # busy time of each kernel: the union of its launches' intervals (launches
+    # on two streams overlap, and each one's duration then includes time the
+    # other stream shares)
     busy_ns = {}
     for k, iv in spans.items():
         total, end = 0, None
@@ -281,7 +325,8 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
              f"--stats-summary {stats_dir}", "",
              f"kernels.hip code sha256 (comments and blank space aside): `{source_hash()}`", "",
              f"{steps_run:.0f} steps traced; bytes per launch = the step's algorithmic bytes for that "
-             f"kernel divided by its launches per step.", "",
+             f"kernel divided by its launches per step. The {n_setup} launches of each sum-of-squares "
+             f"kernel that set up the other ranks' partial sums come first and are left out.", "",
              "Busy us/step is the union of the kernel's launch intervals per step (the same as launches x avg "
              "when launches do not overlap); GB/s (busy) divides the step's bytes for the kernel by it.", "",
              "| kernel | calls | launches/step | avg us | min us | max us | algorithmic bytes/launch | "
@@ -731,6 +776,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_copy_ceiling:
         out["copy_ceiling"] = copy_ceiling(torch, ceiling_elems(call_bytes))
+        if "pack_sqnorm" in algo and not bucketed:
+            # the same copy over the pack's bytes: the ceiling of pack + sum of squares
+            out["copy_ceiling_pack_size"] = copy_ceiling(torch, ceiling_elems(algo["pack_sqnorm"]))
     out.update(baselines)
     print(json.dumps(out), flush=True)
 

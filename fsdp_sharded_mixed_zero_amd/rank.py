@@ -38,6 +38,23 @@ import torch
 from . import synth, zero
 
 
+def other_rank_slices(sizes, shard, rank):
+    """For each tensor that reaches a shard other than ``rank``'s: (tensor
+    index, [(other rank, first element, end element) of the tensor's part in
+    that rank's shard]), in tensor order. RankShard.fill_other_ranks makes one
+    zero_shard_sqnorm call per part."""
+    out, off = [], 0
+    for i, n in enumerate(sizes):
+        if n > 0:
+            r0, r1 = off // shard, (off + n - 1) // shard
+            parts = [(r, max(off, r * shard) - off, min(off + n, (r + 1) * shard) - off)
+                     for r in range(r0, r1 + 1) if r != rank]
+            if parts:
+                out.append((i, parts))
+        off += n
+    return out
+
+
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
                  fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
@@ -156,33 +173,22 @@ class RankShard:
         all-reduce of the ranks' partial sums would deliver ("ZeRO-3 核心流程",
         pitfall 1: the clip norm covers every rank's slice). Set-up work, not
         part of a step: it draws the whole model's gradients once."""
-        wl, S = self.wl, self.shard
+        wl = self.wl
         step = wl.step if step is None else step
         self.rank_sq.zero_()
-        work = [(i, n, off) for i, (n, off) in enumerate(zip(wl.sizes, self._flat_offsets())) if n > 0
-                and not (off // S == self.rank and (off + n - 1) // S == self.rank)]
-        if not work:
+        slices = other_rank_slices(wl.sizes, self.shard, self.rank)
+        if not slices:
             torch.cuda.synchronize(self.device)
             return
-        longest = max(n for _, n, _ in work)
+        longest = max(wl.sizes[i] for i, _ in slices)
         buf = torch.empty(longest, dtype=torch.bfloat16, device=self.device)
         ws = torch.empty((zero.zero_sqnorm_workspace_bytes(longest) + 7) // 8, dtype=torch.float64,
                          device=self.device)
-        for i, n, off in work:
-            g = synth.device_grad_(buf[:n], wl, step, salt=i)
-            for r in range(off // S, (off + n - 1) // S + 1):
-                if r == self.rank:
-                    continue
-                a, b = max(off, r * S) - off, min(off + n, (r + 1) * S) - off
+        for i, parts in slices:
+            g = synth.device_grad_(buf[:wl.sizes[i]], wl, step, salt=i)
+            for r, a, b in parts:
                 zero.zero_shard_sqnorm(g[a:], b - a, self.rank_sq[r:r + 1], True, ws)
         torch.cuda.synchronize(self.device)
-
-    def _flat_offsets(self):
-        out, off = [], 0
-        for n in self.wl.sizes:
-            out.append(off)
-            off += n
-        return out
 
     # --------------------------------------------------------------- step
     def hparams(self, step):

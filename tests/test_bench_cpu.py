@@ -84,35 +84,64 @@ def _write_csv(path, fields, rows):
         w.writerows(rows)
 
 
+NS = "(anonymous namespace)::"
+FINAL = f"{NS}sqnorm_final_kernel(double const*, long, double*, int)"
+PARTIAL = f"{NS}sqnorm_partial_kernel(unsigned short const*, long, long, double*)"
+
+
+def _setup_launches(wl):
+    """The trace rows of the set-up launches (the other ranks' partial sums,
+    one partial and one final kernel each) that precede the first step."""
+    n = bench.setup_sqnorm_launches(wl)
+    rows = []
+    for j in range(n):
+        rows += [{"Kernel_Name": PARTIAL, "Start_Timestamp": 10 * j, "End_Timestamp": 10 * j + 4},
+                 {"Kernel_Name": FINAL, "Start_Timestamp": 10 * j + 5, "End_Timestamp": 10 * j + 9}]
+    return n, rows
+
+
+@needs_lib
+def test_setup_launch_count():
+    """The tiny model's rank 1 of 4 holds tensors 2 and 3: the six others are
+    each in one other rank's shard."""
+    assert bench.setup_sqnorm_launches(synth.WORKLOADS["tiny"]) == 6
+
+
 @needs_lib
 def test_stats_summary_table(tmp_path):
     wl = synth.WORKLOADS["tiny"]
     S = 262_144
-    ns = "(anonymous namespace)::"
-    names = {"adamw": f"void {ns}adamw_vec_kernel<unsigned short>({ns}AdamWArgs)",
-             "pack": f"void {ns}copy_pieces_kernel<true>({ns}CopyPieces, double*)",
-             "unpack": f"void {ns}copy_pieces_kernel<false>({ns}CopyPieces, double*)",
-             "final": f"{ns}sqnorm_final_kernel(double const*, long, double*, int)"}
-    # 12 steps traced; AdamW 2 us per launch, pack and unpack 1 us
-    rows = [{"Name": names["adamw"], "Calls": 12, "AverageNs": 2000, "MinNs": 1900, "MaxNs": 2100},
-            {"Name": names["pack"], "Calls": 12, "AverageNs": 1000, "MinNs": 900, "MaxNs": 1100},
-            {"Name": names["unpack"], "Calls": 12, "AverageNs": 1000, "MinNs": 900, "MaxNs": 1100},
-            {"Name": names["final"], "Calls": 12, "AverageNs": 3000, "MinNs": 2900, "MaxNs": 3100}]
-    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_stats.csv"),
-               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"], rows)
+    names = {"adamw": f"void {NS}adamw_vec_kernel<unsigned short>({NS}AdamWArgs)",
+             "pack": f"void {NS}copy_pieces_kernel<true>({NS}CopyPieces, double*)",
+             "unpack": f"void {NS}copy_pieces_kernel<false>({NS}CopyPieces, double*)",
+             "final": FINAL}
+    # the set-up launches, then 12 steps: AdamW 2 us per launch (1.9 to 2.1),
+    # pack and unpack 1 us, the final sum 3 us
+    n_setup, trace = _setup_launches(wl)
+    dur = {"adamw": 2000, "pack": 1000, "unpack": 1000, "final": 3000}
+    t = 1_000_000
+    for k in range(12):
+        for key, d in dur.items():
+            d = d + (100 if k == 0 else -100 if k == 1 else 0) if key == "adamw" else d
+            trace.append({"Kernel_Name": names[key], "Start_Timestamp": t, "End_Timestamp": t + d})
+            t += d + 500
+    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_trace.csv"),
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
     md = bench.stats_summary(str(tmp_path / "prof"), wl, steps=10, warmup=2, separate_unpack=True)
     assert "--steps 10 --warmup 2 --separate-unpack --no-cpu-baseline --no-copy-ceiling" in md
-    assert "12 steps traced" in md
+    assert "12 steps traced" in md and f"The {n_setup} launches" in md
     table = {line.split("|")[1].strip(): [c.strip() for c in line.split("|")[2:-1]]
              for line in md.splitlines() if line.startswith("| ") and not line.startswith("| kernel |")}
     adamw = table["adamw_vec_kernel<unsigned short>"]
     assert adamw[0] == "12" and adamw[1] == "1.00" and adamw[2] == "2.0"
+    assert adamw[3] == "1.9" and adamw[4] == "2.1"
     assert int(adamw[5]) == 28 * S
     assert float(adamw[6]) == pytest.approx(28 * S / 2e-6 / 1e9, abs=0.1)
     assert float(adamw[7]) == pytest.approx(100 * 28 * S / 2e-6 / 1e9 / 8000, abs=0.1)
+    assert float(adamw[8]) == pytest.approx(2.0)                        # busy us per step
     assert int(table["copy_pieces_kernel<false>"][5]) == 4 * S
-    assert table["sqnorm_final_kernel"][5] == "-"
-    assert adamw[8] == "-"                        # no kernel trace: no busy time
+    final = table["sqnorm_final_kernel"]
+    assert final[0] == "12" and final[2] == "3.0" and final[5] == "-"   # the set-up launches left out
 
 
 def test_stats_summary_busy_time_is_the_union_of_launches(tmp_path):
@@ -120,15 +149,12 @@ def test_stats_summary_busy_time_is_the_union_of_launches(tmp_path):
     of the launch intervals, and the rate over it counts each byte once."""
     wl = synth.WORKLOADS["tiny"]
     S = 262_144
-    ns = "(anonymous namespace)::"
-    adamw = f"void {ns}adamw_vec_kernel<unsigned short>({ns}AdamWArgs)"
-    final = f"{ns}sqnorm_final_kernel(double const*, long, double*, int)"
-    _write_csv(str(tmp_path / "prof" / "x" / "bench_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
-               [{"Name": adamw, "Calls": 4, "AverageNs": 2000, "MinNs": 2000, "MaxNs": 2000},
-                {"Name": final, "Calls": 2, "AverageNs": 100, "MinNs": 100, "MaxNs": 100}])
-    # two steps; in each, two 2 us launches overlapping by 1 us (3 us busy)
-    trace = []
-    for t0 in (0, 10_000):
+    adamw = f"void {NS}adamw_vec_kernel<unsigned short>({NS}AdamWArgs)"
+    final = FINAL
+    # the set-up launches, then two steps; in each, two 2 us launches
+    # overlapping by 1 us (3 us busy)
+    _, trace = _setup_launches(wl)
+    for t0 in (1_000_000, 1_010_000):
         trace += [{"Kernel_Name": adamw, "Start_Timestamp": t0, "End_Timestamp": t0 + 2000},
                   {"Kernel_Name": adamw, "Start_Timestamp": t0 + 1000, "End_Timestamp": t0 + 3000},
                   {"Kernel_Name": final, "Start_Timestamp": t0 + 5000, "End_Timestamp": t0 + 5100}]
@@ -141,13 +167,32 @@ def test_stats_summary_busy_time_is_the_union_of_launches(tmp_path):
     assert float(cells[10]) == pytest.approx(28 * S / 3e-6 / 1e9, abs=0.1)
 
 
-def _counter_csvs(tmp_path, raw):
-    raw = dict(raw, sqnorm_final_kernel=(1.0, 0.0))     # once per step: the trace's step count
+def _counter_csvs(tmp_path, raw, wl, small_copy=None):
+    """Counter rows: the set-up launches first (the other ranks' partial sums:
+    counter values that must not count), then 5 dispatches of each kernel in
+    ``raw`` (grid 1000), the final sum once per step (the step count); with
+    ``small_copy`` (fetch, write), 5 more copy dispatches on a smaller grid
+    (the copy ceiling's copy of the pack's size)."""
+    n_setup = bench.setup_sqnorm_launches(wl)
     for counter, k in (("FETCH_SIZE", 0), ("WRITE_SIZE", 1)):
-        rows = [{"Kernel_Name": f"void (anonymous namespace)::{name}(x)", "Counter_Name": counter,
-                 "Counter_Value": vals[k]} for name, vals in raw.items() for _ in range(5)]
+        rows, d = [], 0
+        for _ in range(n_setup):
+            for name in ("sqnorm_partial_kernel", "sqnorm_final_kernel"):
+                rows.append({"Dispatch_Id": d, "Grid_Size": 64, "Kernel_Name": f"void {NS}{name}(x)",
+                             "Counter_Name": counter, "Counter_Value": 1e9})
+                d += 1
+        for name, vals in dict(raw, sqnorm_final_kernel=(1.0, 0.0)).items():
+            for _ in range(5):
+                rows.append({"Dispatch_Id": d, "Grid_Size": 1000, "Kernel_Name": f"void {NS}{name}(x)",
+                             "Counter_Name": counter, "Counter_Value": vals[k]})
+                d += 1
+        if small_copy:
+            for _ in range(5):
+                rows.append({"Dispatch_Id": d, "Grid_Size": 10, "Kernel_Name": f"void {NS}copy_pieces_kernel<false>(x)",
+                             "Counter_Name": counter, "Counter_Value": small_copy[k]})
+                d += 1
         _write_csv(str(tmp_path / counter / "y" / "bench_counter_collection.csv"),
-                   ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+                   ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
     return str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE")
 
 
@@ -165,7 +210,7 @@ def test_pmc_summary_calibration_from_the_copy_ceiling(tmp_path):
     assert n == 30 * S // 4
     raw = {copy: (2 * n / 1024 / 2, 2 * n / 1024), update: (14 * S / 1024 / 2, 16 * S / 1024),
            "copy_pieces_kernel<true>": (2 * S / 1024 / 2, 2 * S / 1024)}
-    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw), wl, steps=3, warmup=2)
+    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw, wl, small_copy=(7.0, 3.0)), wl, steps=3, warmup=2)
     assert out["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert out["calibration"]["write_factor"] == pytest.approx(1.0)
     assert out["kernels"][update]["algorithmic_bytes"] == 30 * S
@@ -183,7 +228,7 @@ def test_pmc_summary_calibration(tmp_path):
     S = 262_144
     copy, adamw = "copy_pieces_kernel<false>", "adamw_vec_kernel<unsigned short>"
     raw = {copy: (2 * S / 1024 / 2, 2 * S / 1024), adamw: (14 * S / 1024 / 2, 14 * S / 1024 * 1.01)}
-    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw), wl, steps=3, warmup=2, separate_unpack=True)
+    out = bench.pmc_summary(*_counter_csvs(tmp_path, raw, wl), wl, steps=3, warmup=2, separate_unpack=True)
     assert out["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert out["calibration"]["write_factor"] == pytest.approx(1.0)
     assert out["kernels"][copy]["traffic_over_algorithmic"] == pytest.approx(1.0)
