@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into HBM bytes per launch and exit")
+    ap.add_argument("--update-sweep", action="store_true",
+                    help="time the fused update over the first n elements of the workload's shard for several n "
+                         "(20 launches each, events around each) and fit time = fixed + bytes / rate; print "
+                         "markdown and exit")
     ap.add_argument("--stats-summary", metavar="STATS_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run of this benchmark "
                          "(kernel durations, achieved GB/s) as markdown and exit")
@@ -351,6 +355,66 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     return "\n".join(lines) + "\n"
 
 
+def update_sweep(wl, reps=20):
+    """The fused update (zero_adamw_step_unpack) over shard elements [0, n)
+    for n from 1/16 of the shard to all of it, each timed over ``reps``
+    launches with HIP events around each (median), after the breakdown-style
+    warm-up; then a least-squares fit time = fixed + bytes / rate. The fixed
+    part is what a launch costs beyond its bytes: the ramp while the first
+    waves form the clip coefficient and issue their first loads, and the
+    drain while the last waves finish."""
+    import torch
+
+    from fsdp_sharded_mixed_zero_amd import zero
+    from fsdp_sharded_mixed_zero_amd.rank import RankShard
+
+    rs = RankShard(wl)
+    hp = rs.hparams(wl.step)
+    S = rs.shard
+    sizes = sorted({max(zero.ZERO_STATE_TILE, (S * k // 16) // zero.ZERO_STATE_TILE * zero.ZERO_STATE_TILE)
+                    for k in (1, 2, 3, 4, 6, 8, 12, 16)})
+    sizes[-1] = S
+
+    def launch(n):
+        zero.zero_adamw_step_unpack(rs.grad_shard, rs.state, rs.param_shard, S, 0, n, hp, rs.rank_sq, wl.n_d,
+                                    rs.layout, rs.param_ptrs)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < BREAKDOWN_MIN_SECONDS:     # steady clocks
+        for _ in range(10):
+            launch(S)
+        torch.cuda.synchronize()
+    rows = []
+    for n in sizes:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in pairs:
+            e0.record()
+            launch(n)
+            e1.record()
+        torch.cuda.synchronize()
+        us = median([e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs])
+        nbytes = 28 * n + 2 * min(n, rs.real)
+        rows.append((n, nbytes, us))
+    xs = [b for _, b, _ in rows]
+    ys = [t for _, _, t in rows]
+    mx, my = sum(xs) / len(xs), sum(ys) / len(ys)
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    fixed = my - slope * mx
+    lines = [f"# The fused update against its size: {wl.name}, rank {wl.rank} of N_d={wl.n_d}", "",
+             "Command (one MI355X; R is the repository root):", "",
+             f"    cd $R && python3 bench.py --workload {wl.name} --update-sweep", "",
+             f"kernels.hip code sha256 (comments and blank space aside): `{source_hash()}`", "",
+             f"zero_adamw_step_unpack over shard elements [0, n), {reps} launches each, HIP events around each "
+             f"launch, median. Fit: time = {fixed:.1f} us + bytes / {1e-3 / slope:.1f} GB/s "
+             f"({100 * 1e-3 / slope / HBM_PEAK_GBPS:.1f} % of 8 TB/s).", "",
+             "| elements | algorithmic bytes | us | GB/s | % of 8 TB/s | fit us |", "|---|---|---|---|---|---|"]
+    for n, b, us in rows:
+        gbps = b / (us * 1e-6) / 1e9
+        lines.append(f"| {n} | {b} | {us:.1f} | {gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f} | "
+                     f"{fixed + slope * b:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
 def single_launch_calls(rs, fused):
     """Whether every update call of the step is one kernel launch: its range
     is at most ZERO_ADAMW_LAUNCH_ELEMS elements and, for the update with the
@@ -634,6 +698,12 @@ def main():
         from fsdp_sharded_mixed_zero_amd import synth
         print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup,
                             args.accum, args.separate_norm, args.flat, args.separate_unpack), end="")
+        return
+    if args.update_sweep:
+        from fsdp_sharded_mixed_zero_amd import synth
+        import torch
+        torch.cuda.set_device(0)
+        print(update_sweep(synth.WORKLOADS[args.workload]), end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
