@@ -49,6 +49,9 @@ def parse():
                     help="fp32 gradient accumulation over K micro-batches per step (K > 1)")
     ap.add_argument("--separate-unpack", action="store_true",
                     help="run AdamW and the unpack as two calls instead of the fused one")
+    ap.add_argument("--state-arrays", action="store_true",
+                    help="fp32 master, m and v as three separate arrays (zero_adamw_step_arrays), the unpack "
+                         "as its own pass")
     ap.add_argument("--flat", action="store_true",
                     help="ZeRO-1 flat buffers: gradients and parameters are views into flat buffers, the "
                          "shard is the rank's slice (no pack, no unpack)")
@@ -87,9 +90,11 @@ def kernel_name(raw):
     return name.split("(")[0].split("::")[-1]
 
 
-def update_kernel(accum=1, separate_unpack=False, flat=False):
+def update_kernel(accum=1, separate_unpack=False, flat=False, state_arrays=False):
     """The update kernel of a mode (the roofline's dominant kernel)."""
     grad = "float" if accum > 1 else "unsigned short"
+    if state_arrays:
+        return f"adamw_arrays_vec_kernel<{grad}>"
     fused = not separate_unpack and not flat
     return f"adamw_unpack_vec_kernel<{grad}>" if fused else f"adamw_vec_kernel<{grad}>"
 
@@ -100,11 +105,11 @@ def ceiling_elems(launch_bytes):
     return max(8, min(int(launch_bytes), 8 << 30) // 4 // 8 * 8)
 
 
-def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unpack=False):
+def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unpack=False, state_arrays=False):
     """Algorithmic HBM bytes per step of each kernel over the whole shard, for
     the benchmark's mode (fused norm and fused unpack by default, separate
-    norm, separate unpack, fp32 accumulation over ``accum`` micro-batches, or
-    flat buffers)."""
+    norm, separate unpack, fp32 accumulation over ``accum`` micro-batches,
+    flat buffers, or three state arrays with the unpack separate)."""
     from fsdp_sharded_mixed_zero_amd import zero
     info = zero.zero_layout(wl.sizes, wl.n_d, wl.rank, wl.align).info
     S = info["shard"]
@@ -112,7 +117,8 @@ def algorithmic_bytes(wl, accum=1, separate_norm=False, flat=False, separate_unp
     pack = 4 * real + 2 * (S - real)
     if flat:
         return S, real, {"sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel<unsigned short>": 28 * S}
-    update = update_kernel(accum, separate_unpack)
+    separate_unpack = separate_unpack or state_arrays
+    update = update_kernel(accum, separate_unpack, state_arrays=state_arrays)
     out = {}
     if separate_unpack:
         out["copy_pieces_kernel<false>"] = 4 * real          # unpack
@@ -276,7 +282,8 @@ def pmc_summary(fetch_dir, write_dir, wl, steps=20, warmup=2, separate_unpack=Fa
             "kernels": kernels}
 
 
-def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False, separate_unpack=False):
+def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, flat=False, separate_unpack=False,
+                  state_arrays=False):
     """Markdown table of the launches in a rocprofv3 kernel trace of this
     benchmark, with achieved bandwidth from each kernel's algorithmic bytes
     per launch (the step's bytes spread over that kernel's launches per
@@ -284,7 +291,7 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     import csv
     import glob
 
-    S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat, separate_unpack)
+    S, real, algo = algorithmic_bytes(wl, accum, separate_norm, flat, separate_unpack, state_arrays)
     # every launch from the trace, in time order; the set-up launches of the
     # sum-of-squares kernels (the other ranks' partial sums) left out
     spans = {}
@@ -317,7 +324,8 @@ def stats_summary(stats_dir, wl, steps, warmup, accum=1, separate_norm=False, fl
     steps_run = steps_traced({k: int(r["Calls"]) for k, r in rows.items()}, wl, S,
                              combine=accum == 1 and not separate_norm and not flat)
     mode = ((f" --accum {accum}" if accum > 1 else "") + (" --separate-norm" if separate_norm else "") +
-            (" --flat" if flat else "") + (" --separate-unpack" if separate_unpack else ""))
+            (" --flat" if flat else "") + (" --separate-unpack" if separate_unpack else "") +
+            (" --state-arrays" if state_arrays else ""))
     lines = [f"# Kernel durations: {wl.name}, rank {wl.rank} of N_d={wl.n_d} "
              f"(shard {S} elements{f', buckets of {wl.bucket}' if wl.bucket else ''})", "",
              "Commands (one MI355X; R is the repository root):", "",
@@ -697,7 +705,8 @@ def main():
     if args.stats_summary:
         from fsdp_sharded_mixed_zero_amd import synth
         print(stats_summary(args.stats_summary, synth.WORKLOADS[args.workload], args.steps, args.warmup,
-                            args.accum, args.separate_norm, args.flat, args.separate_unpack), end="")
+                            args.accum, args.separate_norm, args.flat, args.separate_unpack, args.state_arrays),
+              end="")
         return
     if args.update_sweep:
         from fsdp_sharded_mixed_zero_amd import synth
@@ -730,7 +739,7 @@ def main():
     if args.offload:
         return offload_main(args, wl)
     rs = RankShard(wl, fused_norm=not args.separate_norm, accum_steps=args.accum, flat=args.flat,
-                   fused_unpack=not args.separate_unpack)
+                   fused_unpack=not args.separate_unpack, state_arrays=args.state_arrays)
     torch.cuda.synchronize()
 
     # Per-phase breakdown first, outside the timed region: events around every
@@ -790,7 +799,8 @@ def main():
     bucketed, n_streams = rs.bucketed, rs.n_streams
     step_bytes = sum(algo.values())
     default_kernel = rs.bucket <= 0 and args.accum == 1 and not args.flat
-    traffic = (measured_traffic(wl.name, update_kernel(args.accum, args.separate_unpack, args.flat))
+    traffic = (measured_traffic(wl.name, update_kernel(args.accum, args.separate_unpack, args.flat,
+                                                       args.state_arrays))
                if default_kernel else None)
 
     out = {
@@ -809,6 +819,8 @@ def main():
         "config": {"workload": f"{wl.name} rank {rs.rank} of N_d={wl.n_d}: one rank's shard, " + (
                                "ZeRO-1 flat buffers: sum of squares -> clip+AdamW+bf16 cast on the rank's slice"
                                if args.flat else
+                               "pack + sum of squares -> clip+AdamW+bf16 cast over three state arrays (master, "
+                               "m, v) -> unpack" if args.state_arrays else
                                "pack -> sum of squares -> clip+AdamW+bf16 cast -> unpack" if args.separate_unpack
                                else "pack + sum of squares -> clip+AdamW+bf16 cast with the unpack fused"),
                    "shard_params": S, "n_d": wl.n_d, "rank": rs.rank, "tensors": len(wl.sizes),
@@ -816,7 +828,8 @@ def main():
                    "bucket": rs.bucket, "streams": rs.n_streams,
                    "norm": "separate" if args.separate_norm or args.flat else "fused into pack",
                    "unpack": ("none (flat buffers)" if args.flat else
-                              "separate" if args.separate_unpack else "fused into AdamW"),
+                              "separate" if args.separate_unpack or args.state_arrays else "fused into AdamW"),
+                   "state": "three arrays" if args.state_arrays else "tiled (master|m|v in 8192-element tiles)",
                    "fp32_grad_accumulation_micro_batches": args.accum if args.accum > 1 else None},
         "adamw_params_per_s": call_elems / (call_ms * 1e-3),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

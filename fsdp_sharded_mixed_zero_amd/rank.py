@@ -23,6 +23,10 @@ accumulation, then the norm and AdamW on the fp32 accumulator ("第 5 课：ZeRO
 与 FSDP" section 2, fp32 gradient accumulation, 4 extra bytes per shard
 element).
 
+With ``state_arrays=True`` the fp32 master, m and v are three separate
+arrays, the form the pages hold the state in ("第 5 课：ZeRO 与 FSDP" section
+2), updated by zero_adamw_step_arrays, with the unpack as its own pass.
+
 With ``flat=True`` the rank holds the ZeRO-1 form (notes on the ZeRO paper,
 section 4.1): the whole gradient and parameter sets live in two flat,
 padded buffers, every tensor is a view into them, and the shard is the rank's
@@ -58,7 +62,8 @@ def other_rank_slices(sizes, shard, rank):
 class RankShard:
     def __init__(self, wl: synth.Workload, rank: int | None = None, device="cuda",
                  fill: bool = True, bucket: int | None = None, fused_norm: bool = True,
-                 accum_steps: int = 1, flat: bool = False, fused_unpack: bool = True, streams: int = 2):
+                 accum_steps: int = 1, flat: bool = False, fused_unpack: bool = True, streams: int = 2,
+                 state_arrays: bool = False):
         self.wl = wl
         self.rank = wl.rank if rank is None else rank
         self.device = torch.device(device)
@@ -75,6 +80,9 @@ class RankShard:
         self.params = [None] * n_t
         dev = self.device
         self.flat = flat
+        if state_arrays and (flat or accum_steps > 1):
+            raise ValueError("three state arrays are used with the packed step without accumulation only")
+        self.state_arrays = state_arrays
         if flat:
             if accum_steps > 1:
                 raise ValueError("flat buffers are not combined with gradient accumulation here")
@@ -100,10 +108,16 @@ class RankShard:
             self.param_shard = torch.empty(S, dtype=torch.bfloat16, device=dev)
         self.grad_ptrs = zero.pointer_array(self.grads)
         self.param_ptrs = zero.pointer_array(self.params)
-        self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
+        if state_arrays:
+            self.state = None
+            self.master, self.m, self.v = (torch.empty(S, dtype=torch.float32, device=dev) for _ in range(3))
+            self._arrays = (self.grad_shard.data_ptr(), self.master.data_ptr(), self.m.data_ptr(),
+                            self.v.data_ptr(), self.param_shard.data_ptr())
+        else:
+            self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
         self.fused_norm = fused_norm
-        self.fused_unpack = fused_unpack and not flat
+        self.fused_unpack = fused_unpack and not flat and not state_arrays
         self.accum_steps = accum_steps
         self.acc = torch.empty(S, dtype=torch.float32, device=dev) if accum_steps > 1 else None
         ws = max(max(zero.zero_sqnorm_workspace_bytes(n),
@@ -134,7 +148,8 @@ class RankShard:
     def fill_state(self, on_chunk=None):
         """Draw master ~ N(0, master_std), m ~ N(0, m_std), v ~ |N(0, v_std)|
         (zeros where the std is 0 and on padding) chunk by chunk as three
-        separate arrays, and import each chunk into the tiled state buffer.
+        separate arrays, and import each chunk into the tiled state buffer
+        (with ``state_arrays``, draw them straight into the three arrays).
         ``on_chunk(lo, hi, master, m, v)`` sees each chunk's separate arrays
         before the import."""
         wl, real, S = self.wl, self.real, self.shard
@@ -146,7 +161,11 @@ class RankShard:
             for buf_id, std, absval in ((synth.MASTER, wl.master_std, False),
                                         (synth.EXP_AVG, wl.m_std, False),
                                         (synth.EXP_AVG_SQ, wl.v_std, True)):
-                x = torch.zeros(n, dtype=torch.float32, device=self.device)
+                if self.state_arrays:
+                    x = {synth.MASTER: self.master, synth.EXP_AVG: self.m, synth.EXP_AVG_SQ: self.v}[buf_id][lo:hi]
+                    x.zero_()
+                else:
+                    x = torch.zeros(n, dtype=torch.float32, device=self.device)
                 r = max(0, min(n, real - lo))
                 if std > 0 and r > 0:
                     synth.device_normal_(x[:r], std, wl.seed, buf_id, abs_value=absval,
@@ -154,7 +173,8 @@ class RankShard:
                 bufs.append(x)
             if on_chunk is not None:
                 on_chunk(lo, hi, *bufs)
-            zero.zero_state_import(*bufs, self.state[3 * lo:], n)
+            if not self.state_arrays:
+                zero.zero_state_import(*bufs, self.state[3 * lo:], n)
         torch.cuda.synchronize()
 
     def fill_grads(self, step):
@@ -257,11 +277,20 @@ class RankShard:
                     self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
                     self.wl.n_d, self.layout, self.param_ptrs, stream))
                 continue
-            mark("adamw", lambda: zero.zero_adamw_step(
-                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
-                self.wl.n_d, stream))
+            mark("adamw", lambda: self._adamw(b, n, hp, stream))
             mark("unpack", lambda: zero.zero_unpack_params(self.layout, self.param_shard, self.param_ptrs,
                                                           b, n, stream))
+
+    def _adamw(self, b, n, hp, stream):
+        """The update of shard elements [b, b+n) without the unpack: over the
+        tiled state, or over the three state arrays (offset pointers)."""
+        if self.state_arrays:
+            g, p, m, v, o = self._arrays
+            zero.zero_adamw_step_arrays(g + 2 * b, p + 4 * b, m + 4 * b, v + 4 * b, o + 2 * b, n, hp,
+                                        self.rank_sq, self.wl.n_d, stream)
+            return
+        zero.zero_adamw_step(self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
+                             self.wl.n_d, stream)
 
     def pack_norm_buckets(self, own, stream):
         """Pack + sum of squares of every bucket on the step's streams in turn,
@@ -320,8 +349,7 @@ class RankShard:
                 self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq, self.wl.n_d,
                 self.layout, self.param_ptrs, st)))
         else:
-            timed("adamw", lambda: on_streams(lambda b, n, st: zero.zero_adamw_step(
-                self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq, self.wl.n_d, st)))
+            timed("adamw", lambda: on_streams(lambda b, n, st: self._adamw(b, n, hp, st)))
             timed("unpack", lambda: on_streams(lambda b, n, st: zero.zero_unpack_params(
                 self.layout, self.param_shard, self.param_ptrs, b, n, st)))
 

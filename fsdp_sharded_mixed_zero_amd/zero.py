@@ -95,6 +95,8 @@ _SIGNATURES = {
     "zero_adamw_step_f32grad_unpack": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                                       ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP,
                                                       ctypes.POINTER(_VP), _VP]),
+    "zero_adamw_step_arrays": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64,
+                                              ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _VP]),
     "zero_accumulate_grads": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
     "zero_cpu_adamw_step": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64,
                                            ctypes.POINTER(zero_adamw_hparams), _VP, _I32, _I32]),
@@ -366,6 +368,20 @@ def zero_adamw_step(grad, state, param, n_state: int, begin: int, count: int, hp
     _need_update(grad, 2, state, param, n_state, begin, count, rank_sqnorms, n_ranks)
     _check("zero_adamw_step", library().zero_adamw_step(
         _ptr(grad), _ptr(state), _ptr(param), n_state, begin, count, ctypes.byref(hp),
+        _ptr(rank_sqnorms), n_ranks, _stream(stream)))
+
+
+def zero_adamw_step_arrays(grad, master, m, v, param, count: int, hp: zero_adamw_hparams, rank_sqnorms,
+                           n_ranks: int, stream=None):
+    if count > 0:
+        _need(grad, 2 * count, "gradient")
+        for x, what in ((master, "master"), (m, "m"), (v, "v")):
+            _need(x, 4 * count, what)
+        _need(param, 2 * count, "parameter shard")
+        if n_ranks > 0:
+            _need(rank_sqnorms, 8 * n_ranks, "rank sums of squares")
+    _check("zero_adamw_step_arrays", library().zero_adamw_step_arrays(
+        _ptr(grad), _ptr(master), _ptr(m), _ptr(v), _ptr(param), count, ctypes.byref(hp),
         _ptr(rank_sqnorms), n_ranks, _stream(stream)))
 
 

@@ -363,6 +363,31 @@ int zero_adamw_step_unpack(const uint16_t* d_grad, float* d_state, uint16_t* d_p
                            const double* d_rank_sqnorms, int32_t n_ranks, zero_layout_t h,
                            uint16_t* const* tensor_params, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * zero_adamw_step_arrays -- zero_adamw_step over the state as the pages hold
+ * it: the fp32 master weights, m and v of the rank's slice as three separate
+ * arrays, K = 12 bytes per parameter ("第 5 课：ZeRO 与 FSDP" sections 2-3;
+ * notes on the ZeRO paper, sections 2.1 and 4.1). The arithmetic, the clip
+ * coefficient and the rounding rule are zero_adamw_step's; the results are
+ * bit-identical to it on the same values.
+ *   d_grad    device pointer to count bf16 gradients
+ *   d_master, d_m, d_v  device pointers to count fp32 values each; updated in
+ *             place
+ *   d_param   device pointer to count bf16 parameters (written)
+ *   count     elements; a sub-range of larger arrays is passed as offset
+ *             pointers
+ *   hp, d_rank_sqnorms, n_ranks, stream  as zero_adamw_step
+ * When the five pointers share one phase (master, m and v equally placed
+ * against 16-byte boundaries, and the gradient and parameter against 8-byte
+ * boundaries at the same element), the update takes the vector path; other
+ * placements take a slower element path with identical results. More than
+ * 2^27 elements take several launches on `stream`.
+ * Errors: as zero_adamw_step; also ZERO_EINVAL when any two of the five
+ * arrays overlap, or for a NULL or non-4-byte-aligned m or v with count > 0. */
+int zero_adamw_step_arrays(const uint16_t* d_grad, float* d_master, float* d_m, float* d_v,
+                           uint16_t* d_param, int64_t count, const zero_adamw_hparams* hp,
+                           const double* d_rank_sqnorms, int32_t n_ranks, hipStream_t stream);
+
 /* zero_state_import / zero_state_export -- copy n elements of fp32 master, m
  * and v between three separate device arrays and the tiled state buffer
  * (layout above). A bit copy; the arrays must not overlap. For callers whose

@@ -21,5 +21,6 @@ int zero_shard_sqnorm_f32(const float*, int64_t, double*, int32_t, void*, size_t
 int zero_adamw_step_f32grad(const float*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, hipStream_t) { return -1; }
 int zero_adamw_step_unpack(const uint16_t*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, zero_layout_t, uint16_t* const*, hipStream_t) { return -1; }
 int zero_adamw_step_f32grad_unpack(const float*, float*, uint16_t*, int64_t, int64_t, int64_t, const zero_adamw_hparams*, const double*, int32_t, zero_layout_t, uint16_t* const*, hipStream_t) { return -1; }
+int zero_adamw_step_arrays(const uint16_t*, float*, float*, float*, uint16_t*, int64_t, const zero_adamw_hparams*, const double*, int32_t, hipStream_t) { return -1; }
 int zero_unpack_params(zero_layout_t, const uint16_t*, uint16_t* const*, int64_t, int64_t, hipStream_t) { return -1; }
 }

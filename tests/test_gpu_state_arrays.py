@@ -1,0 +1,284 @@
+"""The update over three separate state arrays (zero_adamw_step_arrays): the
+fp32 master, m and v as the pages hold them ("第 5 课：ZeRO 与 FSDP" section 2,
+K = 12 bytes per parameter as three states).
+
+Checked against the oracle element by element, and bit for bit against the
+tiled update (zero_adamw_step) on the same values:
+  * every phase of the arrays (offset pointers 0-3 elements into their
+    buffers), ragged counts from 1 element to several thousand units;
+  * arrays in different phases (the element path);
+  * a range cut into two launches, with a phase;
+  * masters planted at cancellation points;
+  * the 7.5B shard at full size in the benchmark's step (RankShard with
+    state_arrays), against the default step;
+and the refusals (overlapping arrays, NULL or misaligned m or v). Guard
+elements around every buffer must keep their values: the kernel addresses
+each launch from an element before the first when the phase is not 0.
+"""
+
+import numpy as np
+import pytest
+
+from fsdp_sharded_mixed_zero_amd import synth, zero
+from oracle import step as O
+from state_tiles import from_tiles, to_tiles
+from tolerance import assert_bf16_param, assert_f32_state
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GUARD = 4
+F32_GUARD = np.uint32(0x7FC0DEAD)   # a NaN with a payload
+BF16_GUARD = np.uint16(synth.SENTINEL)
+
+
+def hp_of(ohp, step):
+    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
+                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm,
+                        clip_eps=ohp.clip_eps, step=step)
+
+
+def guarded(values, offset):
+    """A device buffer holding ``values`` from element GUARD + offset, guard
+    patterns before and after; returns (buffer, view of the values)."""
+    n = values.size
+    if values.dtype == np.float32:
+        buf = np.full(2 * GUARD + offset + n, F32_GUARD, np.uint32)
+        buf[GUARD + offset:GUARD + offset + n] = values.view(np.uint32)
+        d = torch.from_numpy(buf.view(np.int32)).to(DEV).view(torch.float32)
+    else:
+        buf = np.full(2 * GUARD + offset + n, BF16_GUARD, np.uint16)
+        buf[GUARD + offset:GUARD + offset + n] = values
+        d = torch.from_numpy(buf.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return d, d[GUARD + offset:GUARD + offset + n]
+
+
+def host_bits(t):
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_guards(buf, offset, n):
+    b = host_bits(buf)
+    pat = F32_GUARD if buf.dtype == torch.float32 else BF16_GUARD
+    assert (b[:GUARD + offset] == pat).all(), "guard before the array changed"
+    assert (b[GUARD + offset + n:] == pat).all(), "guard after the array changed"
+
+
+def inputs(n, seed, m_std=1e-4, v_std=1e-8):
+    rng = np.random.default_rng(seed)
+    bits = synth.to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * m_std).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * v_std).astype(np.float32)
+    return bits, master, m, v
+
+
+def tiled_twin(bits, master, m, v, hp, d_parts, n_ranks):
+    """The tiled update of the same values: (master, m, v, param) on the host."""
+    n = bits.size
+    d_s = torch.from_numpy(to_tiles(master, m, v)).to(DEV)
+    d_o = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    d_g = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    zero.zero_adamw_step(d_g, d_s, d_o, n, 0, n, hp, d_parts, n_ranks)
+    tm, tmm, tv = from_tiles(d_s.cpu().numpy(), n)
+    return tm, tmm, tv, host_bits(d_o)
+
+
+def arrays_case(n, offsets, step=3, ohp=None, n_ranks=4, seed=0, m_std=1e-4, v_std=1e-8):
+    """Update n elements held at ``offsets`` = (grad, master, m, v, param)
+    elements into their buffers; compare with the tiled update (bit for bit)
+    and the oracle."""
+    ohp = ohp or O.AdamWHParams()
+    bits, master, m, v = inputs(n, seed, m_std, v_std)
+    parts = np.abs(np.random.default_rng(seed + 1).standard_normal(n_ranks)) * 3e-4 * n
+    d_parts = torch.from_numpy(parts).to(DEV)
+    og, op, om, ov, oo = offsets
+    bg, g = guarded(bits, og)
+    bp, p = guarded(master, op)
+    bm, mm = guarded(m, om)
+    bv, vv = guarded(v, ov)
+    bo, o = guarded(np.zeros(n, np.uint16), oo)
+    hp = hp_of(ohp, step)
+    zero.zero_adamw_step_arrays(g, p, mm, vv, o, n, hp, d_parts, n_ranks)
+    for buf, off in ((bg, og), (bp, op), (bm, om), (bv, ov), (bo, oo)):
+        check_guards(buf, off, n)
+    assert np.array_equal(host_bits(g), bits), "the gradient changed"
+    got = [host_bits(x) for x in (p, mm, vv)] + [host_bits(o)]
+    twin = tiled_twin(bits, master, m, v, hp, d_parts, n_ranks)
+    for name, a, b in zip(("master", "m", "v", "param"), got, twin):
+        bb = b.view(np.uint32) if b.dtype == np.float32 else b
+        assert np.array_equal(a, bb), f"{name}: the three-array update differs from the tiled one"
+    coef = O.clip_coef(O.global_sqnorm(parts), ohp.max_norm, ohp.clip_eps)
+    want = O.adamw_step(bits, master, m, v, step, ohp, coef)
+    g_master, g_m, g_v = (x.view(np.float32) for x in got[:3])
+    assert_f32_state(g_master, want[0], "master")
+    assert_f32_state(g_m, want[1], "m", m)
+    assert_f32_state(g_v, want[2], "v", v)
+    assert_bf16_param(got[3], want[3], want[0], "param", g_master)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 63, 64, 65, 1000, 8197, 3 * 8192 + 6, 300_001])
+@pytest.mark.parametrize("phase", [0, 1, 2, 3])
+def test_arrays_every_phase(n, phase):
+    arrays_case(n, (phase,) * 5, seed=n + phase)
+
+
+@pytest.mark.parametrize("offsets", [(0, 1, 2, 3, 0), (1, 0, 0, 0, 1), (0, 0, 0, 0, 1), (2, 2, 2, 1, 2),
+                                     (3, 3, 3, 3, 0)])
+def test_arrays_mixed_phases_take_the_element_path(offsets):
+    arrays_case(100_003, offsets, seed=sum(offsets))
+
+
+@pytest.mark.parametrize("step,n_ranks,max_norm", [(1, 1, 1.0), (1000, 64, 1.0), (2, 65, 1.0), (5, 3, 0.0)])
+def test_arrays_steps_ranks_clip(step, n_ranks, max_norm):
+    arrays_case(65_536 + 5, (1,) * 5, step=step, ohp=O.AdamWHParams(max_norm=max_norm), n_ranks=n_ranks,
+                seed=step + n_ranks)
+
+
+def test_arrays_first_step_from_zero_state():
+    arrays_case(100_000, (0,) * 5, step=1, m_std=0.0, v_std=0.0, seed=1)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_arrays_cancellation(kind):
+    """Masters planted at cancellation points: the three-array update takes
+    the same fp64 recompute as the tiled one, bit for bit."""
+    from cancellation_inputs import planted
+
+    n = (1 << 20) + 77
+    bits, master, m, v, step, G, deep, size = planted(n, 9, kind)
+    hp = hp_of(O.AdamWHParams(), step)
+    rs = torch.tensor([G], dtype=torch.float64, device=DEV)
+    d = [torch.from_numpy(x.copy()).to(DEV) for x in (master, m, v)]
+    g = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    o = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    zero.zero_adamw_step_arrays(g, *d, o, n, hp, rs, 1)
+    twin = tiled_twin(bits, master, m, v, hp, rs, 1)
+    assert deep.sum() > 1000
+    for name, a, b in zip(("master", "m", "v"), d, twin[:3]):
+        assert np.array_equal(host_bits(a), b.view(np.uint32)), name
+    assert np.array_equal(host_bits(o), twin[3])
+
+
+def test_arrays_range_in_two_launches():
+    """2^27 + 4099 elements at phase 3: two launches, the first addressed from
+    three elements before the arrays. Every element against the tiled update
+    (its own launch cut elsewhere), windows at both ends and around both cuts
+    against the oracle."""
+    n = (1 << 27) + 4099
+    phase = 3
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2027)
+    bufs = {}
+    for name, std, dt in (("g", 1e-3, torch.bfloat16), ("p", 0.02, torch.float32), ("m", 1e-4, torch.float32),
+                          ("v", 1e-8, torch.float32)):
+        b = torch.empty(n + 2 * GUARD + phase, dtype=dt, device=DEV)
+        b.view(torch.int16 if dt == torch.bfloat16 else torch.int32).fill_(
+            int(BF16_GUARD) if dt == torch.bfloat16 else int(F32_GUARD))
+        x = torch.randn(n, generator=gen, device=DEV) * std
+        if name == "v":
+            x.abs_()
+        b[GUARD + phase:GUARD + phase + n].copy_(x)
+        bufs[name] = b
+    bo = torch.empty(n + 2 * GUARD + phase, dtype=torch.int16, device=DEV).fill_(int(BF16_GUARD))
+    bo = bo.view(torch.bfloat16)
+    view = {k: b[GUARD + phase:GUARD + phase + n] for k, b in bufs.items()}
+    o = bo[GUARD + phase:GUARD + phase + n]
+    # the three-array launches cut at element 2^26 + 8192 - 3 (launch element
+    # 0 sits 3 before the arrays), the tiled ones at 2^26 + 8192
+    cut = (1 << 26) + 8192
+    windows = [(0, 4096), (cut - 3 - 2048, cut - 3 + 2048), (cut - 1024, cut + 3072), (n - 4096, n)]
+    before = {k: [view[k][a:b].clone() for a, b in windows] for k in ("g", "p", "m", "v")}
+    ohp = O.AdamWHParams()
+    hp = hp_of(ohp, 7)
+    parts = torch.tensor([0.5, 0.25], dtype=torch.float64, device=DEV)
+    d_s = torch.empty(3 * n, dtype=torch.float32, device=DEV)
+    zero.zero_state_import(view["p"], view["m"], view["v"], d_s, n)
+    d_o = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    zero.zero_adamw_step(view["g"], d_s, d_o, n, 0, n, hp, parts, 2)
+    zero.zero_adamw_step_arrays(view["g"], view["p"], view["m"], view["v"], o, n, hp, parts, 2)
+    torch.cuda.synchronize()
+    for b in list(bufs.values()) + [bo]:
+        check_guards(b, phase, n)
+    exported = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(3)]
+    zero.zero_state_export(d_s, *exported, n)
+    for k, t in zip(("p", "m", "v"), exported):
+        assert torch.equal(view[k].view(torch.int32), t.view(torch.int32)), k
+    assert torch.equal(o.view(torch.int16), d_o.view(torch.int16))
+    del d_s, exported, d_o
+    coef = O.clip_coef(O.global_sqnorm([0.5, 0.25]), ohp.max_norm, ohp.clip_eps)
+    for w, (a, b) in enumerate(windows):
+        gb = host_bits(before["g"][w])
+        mst, mm, vv = (before[k][w].cpu().numpy() for k in ("p", "m", "v"))
+        want = O.adamw_step(gb, mst, mm, vv, 7, ohp, coef)
+        got_p = view["p"][a:b].cpu().numpy()
+        assert_f32_state(got_p, want[0], f"master window {w}")
+        assert_f32_state(view["m"][a:b].cpu().numpy(), want[1], f"m window {w}", mm)
+        assert_f32_state(view["v"][a:b].cpu().numpy(), want[2], f"v window {w}", vv)
+        assert_bf16_param(host_bits(o[a:b]), want[3], want[0], f"param window {w}", got_p)
+    del bufs, bo, view, o
+    torch.cuda.empty_cache()
+
+
+def test_arrays_full_shard_step_matches_the_default_step():
+    """The 7.5B shard (rank 1 of 64, 119.4 M elements) in the benchmark's
+    step with three state arrays (pack + sum of squares, the three-array
+    update, the unpack) against the default step (the update over the tiled
+    state with the unpack fused), bit for bit: state, parameter shard and
+    every tensor the shard touches, over two steps. The default step is
+    compared with the oracle at every element of this shard elsewhere."""
+    from fsdp_sharded_mixed_zero_amd.rank import RankShard
+
+    wl = synth.WORKLOADS["gpt-7.5b"]
+    print(f"\n[state arrays {wl.name} rank {wl.rank}]", flush=True)
+    a = RankShard(wl, state_arrays=True)
+    b = RankShard(wl)
+    for t in (wl.step, wl.step + 1):
+        a.fill_grads(t)
+        b.fill_grads(t)
+        a.step(t)
+        b.step(t)
+    torch.cuda.synchronize()
+    S = a.shard
+    exported = [torch.empty(S, dtype=torch.float32, device=DEV) for _ in range(3)]
+    zero.zero_state_export(b.state, *exported, S)
+    for name, x, y in zip(("master", "m", "v"), (a.master, a.m, a.v), exported):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), name
+    assert torch.equal(a.param_shard.view(torch.int16), b.param_shard.view(torch.int16))
+    for x, y in zip(a.params, b.params):
+        if x is not None:
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(a.rank_sq, b.rank_sq)
+    print(f"[state arrays {wl.name}] two steps bit-identical to the default step", flush=True)
+    del a, b, exported
+    torch.cuda.empty_cache()
+
+
+def test_arrays_refusals():
+    n = 1000
+    f = [torch.zeros(n + 8, dtype=torch.float32, device=DEV) for _ in range(3)]
+    g = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    o = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    hp = hp_of(O.AdamWHParams(max_norm=0.0), 1)
+    ok = (g, f[0], f[1], f[2], o)
+    zero.zero_adamw_step_arrays(*ok, n, hp, None, 0)                  # valid
+    zero.zero_adamw_step_arrays(None, None, None, None, None, 0, hp, None, 0)   # empty: nothing to do
+    bad = [
+        (g, f[0], f[0], f[2], o),                                        # master and m the same
+        (g, f[0], f[1], f[1][3:], o),                                    # m and v overlap
+        (g, f[0], f[1], f[2], f[2].view(torch.bfloat16)),                # param inside v
+        (g, f[0], f[1], f[2], g),                                        # param is the gradient
+        (g, f[0], None, f[2], o),                                        # NULL m
+        (g, f[0], f[1], f[2].data_ptr() + 2, o),                         # v not 4-byte aligned
+    ]
+    for args in bad:
+        with pytest.raises(zero.ZeroError):
+            zero.zero_adamw_step_arrays(*args, n, hp, None, 0)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_adamw_step_arrays(*ok, -1, hp, None, 0)
+    with pytest.raises(zero.ZeroError):
+        zero.zero_adamw_step_arrays(*ok, n, hp_of(O.AdamWHParams(), 1), None, 0)   # clipping without sums
+    torch.cuda.synchronize()
