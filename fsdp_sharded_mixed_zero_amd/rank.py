@@ -111,8 +111,6 @@ class RankShard:
         if state_arrays:
             self.state = None
             self.master, self.m, self.v = (torch.empty(S, dtype=torch.float32, device=dev) for _ in range(3))
-            self._arrays = (self.grad_shard.data_ptr(), self.master.data_ptr(), self.m.data_ptr(),
-                            self.v.data_ptr(), self.param_shard.data_ptr())
         else:
             self.state = torch.empty(3 * S, dtype=torch.float32, device=dev)
         self.rank_sq = torch.zeros(wl.n_d, dtype=torch.float64, device=dev)
@@ -285,9 +283,11 @@ class RankShard:
         """The update of shard elements [b, b+n) without the unpack: over the
         tiled state, or over the three state arrays (offset pointers)."""
         if self.state_arrays:
-            g, p, m, v, o = self._arrays
-            zero.zero_adamw_step_arrays(g + 2 * b, p + 4 * b, m + 4 * b, v + 4 * b, o + 2 * b, n, hp,
-                                        self.rank_sq, self.wl.n_d, stream)
+            # addresses read at each call: the arrays may be rebound (a restored checkpoint)
+            zero.zero_adamw_step_arrays(self.grad_shard.data_ptr() + 2 * b, self.master.data_ptr() + 4 * b,
+                                        self.m.data_ptr() + 4 * b, self.v.data_ptr() + 4 * b,
+                                        self.param_shard.data_ptr() + 2 * b, n, hp, self.rank_sq, self.wl.n_d,
+                                        stream)
             return
         zero.zero_adamw_step(self.grad_shard, self.state, self.param_shard, self.shard, b, n, hp, self.rank_sq,
                              self.wl.n_d, stream)

@@ -4,7 +4,10 @@ ZeRO 與 FSDP", on sharded checkpoints). Ten steps straight through must equal,
 bit for bit, five steps, a save of the shard (zero_state_export to three
 arrays, written to .npy files), a fresh state buffer filled with garbage, a
 load (zero_state_import), and five more steps: the state, the bf16 parameter
-shard and the per-tensor parameters. Each step draws fresh gradients."""
+shard and the per-tensor parameters. Each step draws fresh gradients. With
+the state held as three arrays (master, m, v: the pages' own form), the
+shard is saved as those arrays and the rank's arrays are replaced by the
+loaded ones."""
 
 import numpy as np
 import pytest
@@ -53,3 +56,33 @@ def test_resume_from_sharded_checkpoint(name, tmp_path):
         if a is not None:
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     print(f"[checkpoint {name}] ten steps == five + save/load + five, bit for bit", flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2-1.5b"])
+def test_resume_three_state_arrays(name, tmp_path):
+    from fsdp_sharded_mixed_zero_amd import synth
+    from fsdp_sharded_mixed_zero_amd.rank import RankShard
+
+    wl = synth.WORKLOADS[name]
+    print(f"\n[checkpoint {name}, three state arrays]", flush=True)
+    straight = RankShard(wl, state_arrays=True)
+    _run(straight, 10, wl.step)
+
+    resumed = RankShard(wl, state_arrays=True)
+    _run(resumed, 5, wl.step)
+    names = ("master", "m", "v")
+    for k in names:
+        np.save(tmp_path / f"rank{resumed.rank}_{k}.npy", getattr(resumed, k).cpu().numpy())
+        setattr(resumed, k, None)
+    torch.cuda.empty_cache()
+    for k in names:
+        setattr(resumed, k, torch.from_numpy(np.load(tmp_path / f"rank{resumed.rank}_{k}.npy")).to("cuda"))
+    _run(resumed, 5, wl.step + 5)
+
+    for k in names:
+        assert torch.equal(getattr(straight, k).view(torch.int32), getattr(resumed, k).view(torch.int32)), k
+    assert torch.equal(straight.param_shard.view(torch.int16), resumed.param_shard.view(torch.int16))
+    for a, b in zip(straight.params, resumed.params):
+        if a is not None:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    print(f"[checkpoint {name}, three state arrays] ten steps == five + save/load + five, bit for bit", flush=True)
