@@ -376,7 +376,9 @@ int zero_adamw_step_unpack(const uint16_t* d_grad, float* d_state, uint16_t* d_p
  *   d_param   device pointer to count bf16 parameters (written)
  *   count     elements; a sub-range of larger arrays is passed as offset
  *             pointers
- *   hp, d_rank_sqnorms, n_ranks, stream  as zero_adamw_step
+ *   hp, d_rank_sqnorms, n_ranks, stream  as zero_adamw_step; a caller that
+ *             holds the already-combined global sum of squares G passes a
+ *             one-element array holding G with n_ranks = 1
  * When the five pointers share one phase (master, m and v equally placed
  * against 16-byte boundaries, and the gradient and parameter against 8-byte
  * boundaries at the same element), the update takes the vector path; other
