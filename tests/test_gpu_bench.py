@@ -48,3 +48,24 @@ def test_bench_json_line():
     assert d["cpu_baseline"]["cores"] == 1
     assert d["copy_ceiling"]["copied_correctly"] is True and d["copy_ceiling"]["GBps"] > 0
     print(f"[bench tiny] {d['ms_per_step']:.4f} ms per step", flush=True)
+
+
+@pytest.mark.parametrize("mode,kernels,update_bytes", [
+    ("--state-arrays", {"pack_sqnorm", "adamw", "unpack"}, 28),
+    ("--separate-unpack", {"pack_sqnorm", "adamw", "unpack"}, 28),
+    ("--flat", {"sqnorm", "adamw"}, 28),
+])
+def test_bench_modes(mode, kernels, update_bytes):
+    """The other step forms of the benchmark on the tiny workload: the line's
+    phases and the update's bytes per element."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3", "--warmup", "1",
+           "--no-cpu-baseline", "--no-copy-ceiling", mode]
+    print(f"\n[bench tiny {mode}]", flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert set(d["kernels"]) == kernels
+    S = d["config"]["shard_params"]
+    assert d["roofline"]["algorithmic_bytes_per_launch"] == update_bytes * S
+    if mode == "--state-arrays":
+        assert d["config"]["state"] == "three arrays" and d["config"]["unpack"] == "separate"
