@@ -60,6 +60,11 @@ def test_algorithmic_bytes_modes():
                  "sqnorm_f32_partial_kernel": 4 * S, "adamw_vec_kernel<float>": 30 * S}
     _, _, b = bench.algorithmic_bytes(wl, flat=True)
     assert b == {"sqnorm_partial_kernel": 2 * S, "adamw_vec_kernel<unsigned short>": 28 * S}
+    # three state arrays: the unpack is its own pass
+    _, _, b = bench.algorithmic_bytes(wl, state_arrays=True)
+    assert b == {"copy_pieces_kernel<false>": 4 * S, "copy_pieces_kernel<true>": 4 * S,
+                 "adamw_arrays_vec_kernel<unsigned short>": 28 * S}
+    assert bench.update_kernel(state_arrays=True) == "adamw_arrays_vec_kernel<unsigned short>"
 
 
 @needs_lib
