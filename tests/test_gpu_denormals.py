@@ -12,6 +12,7 @@ from fsdp_sharded_mixed_zero_amd import zero
 from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import TILE, from_tiles, to_tiles
+from devbits import hp_of, u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -19,20 +20,10 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda")
 
 
-def hp_of(ohp, step):
-    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
-                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm,
-                        clip_eps=ohp.clip_eps, step=step)
-
-
 def dev_grad(grad):
     if grad.dtype == np.float32:
         return torch.from_numpy(grad.copy()).to(DEV)
     return torch.from_numpy(grad.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("f32grad", [False, True], ids=["bf16-grad", "f32-grad"])

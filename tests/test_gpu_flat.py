@@ -8,13 +8,10 @@ import numpy as np
 import pytest
 
 from fsdp_sharded_mixed_zero_amd import synth
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("name,rank", [("tiny", 1), ("tiny", 3), ("gpt2-1.5b", 63), ("gpt-7.5b", 1), ("llama-7b", 3)])

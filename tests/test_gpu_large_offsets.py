@@ -10,6 +10,7 @@ import pytest
 
 from fsdp_sharded_mixed_zero_amd import synth, zero
 from oracle.layout import build_layout
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -21,10 +22,6 @@ RANGES = [((1 << 31) - 100, 1000), ((1 << 31) + 7, 4099), (N - 1000, 1000), (3, 
 
 def pattern(lo, hi):
     return (np.arange(lo, hi, dtype=np.int64) & 0xFFFF).astype(np.uint16)
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 @pytest.fixture(scope="module")

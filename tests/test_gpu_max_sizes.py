@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 from fsdp_sharded_mixed_zero_amd import synth, zero
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -39,10 +40,6 @@ def pattern(lo, hi):
 
 def other(lo, hi):
     return (0x4000 + (np.arange(lo, hi, dtype=np.int64) & 63)).astype(np.uint16)
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def put(t, lo, bits):

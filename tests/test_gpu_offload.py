@@ -11,13 +11,10 @@ from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import from_tiles, to_tiles
 from tolerance import assert_bf16_param, assert_f32_state, assert_norm_close
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("name,bucket", [("tiny", 65_536), ("tiny", 100_003), ("gpt2-1.5b", 1 << 22),

@@ -11,6 +11,7 @@ from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import TILE, from_tiles, to_tiles
 from tolerance import assert_bf16_close, assert_bf16_param, assert_f32_state, assert_norm_close
+from devbits import hp_of
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -32,12 +33,6 @@ def to_dev_f32(x):
 
 def sentinel(n):
     return torch.full((n,), synth.SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-
-
-def hp_of(ohp, step):
-    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
-                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm,
-                        clip_eps=ohp.clip_eps, step=step)
 
 
 def sqnorm_dev(grad_view, count, accumulate=False, out=None):

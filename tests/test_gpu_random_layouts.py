@@ -19,6 +19,7 @@ from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import from_tiles, to_tiles
 from tolerance import assert_bf16_param, assert_f32_state
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,10 +61,6 @@ def device_tensors(host, offsets):
         views.append(buf[PAD + off:PAD + off + len(x)].view(torch.bfloat16))
         bufs.append(buf)
     return views, bufs
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def shard_positions(lay, shard_bits, sizes, b, c):

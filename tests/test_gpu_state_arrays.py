@@ -23,6 +23,7 @@ from fsdp_sharded_mixed_zero_amd import synth, zero
 from oracle import step as O
 from state_tiles import from_tiles, to_tiles
 from tolerance import assert_bf16_param, assert_f32_state
+from devbits import hp_of
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -31,12 +32,6 @@ DEV = "cuda"
 GUARD = 4
 F32_GUARD = np.uint32(0x7FC0DEAD)   # a NaN with a payload
 BF16_GUARD = np.uint16(synth.SENTINEL)
-
-
-def hp_of(ohp, step):
-    return zero.hparams(lr=ohp.lr, beta1=ohp.beta1, beta2=ohp.beta2, eps=ohp.eps,
-                        weight_decay=ohp.weight_decay, max_norm=ohp.max_norm,
-                        clip_eps=ohp.clip_eps, step=step)
 
 
 def guarded(values, offset):

@@ -27,15 +27,12 @@ from oracle.layout import build_layout
 from other_ranks import check_library_partials, oracle_rank_partial, torch_rank_partials
 from state_tiles import from_tiles
 from tolerance import assert_bf16_param, assert_f32_state, assert_norm_close
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 PIECE = 1 << 23
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def oracle_update(grad_bits, master, m, v, step, ohp, coef):

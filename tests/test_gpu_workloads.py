@@ -32,15 +32,12 @@ from oracle import step as O
 from oracle.layout import build_layout
 from state_tiles import state_range
 from tolerance import assert_bf16_param, assert_f32_state, assert_norm_close
+from devbits import u16
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 SAMPLE = 1 << 16
-
-
-def u16(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 class DeviceTensor:
