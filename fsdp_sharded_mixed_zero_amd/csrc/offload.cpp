@@ -87,30 +87,58 @@ inline float widen(uint16_t h) {
 #define ZERO_HOST_CLONES
 #endif
 
+// One element: the update in place and its bf16 parameter.
+inline uint16_t adam_one(const HostAdam& a, uint16_t gbits, float& p, float& m, float& v) {
+  const float gj = widen(gbits);
+  const float gh = gj * a.coef;
+  const float mg = a.omb1 * gh;
+  const float mj = std::fma(a.beta1, m, mg);
+  const float vj = std::fma(a.beta2, v, a.omb2 * (gh * gh));
+  const float denom = std::fma(std::sqrt(vj), a.inv_sqrt_bc2, a.eps);
+  const float pd = std::fma(-a.lr_wd, p, p);
+  const float pj = std::fma(-a.step_size, mj / denom, pd);
+  if (std::fma(-kCancel, std::fabs(pd), std::fabs(pj)) * denom <
+      (kCancel * a.step_size) * (std::fabs(a.beta1 * m) + std::fabs(mg))) {
+    adam_exact(a, gj, p, m, v);
+  } else {
+    m = mj;
+    v = vj;
+    p = pj;
+  }
+  return bf16_rne(p);
+}
+
+typedef uint16_t u16x32 __attribute__((vector_size(64)));
+
+// A 64-byte line to a 64-byte aligned address, non-temporal where the
+// compiler has the builtin (clang); GCC stores it plainly.
+inline void store_line(uint16_t* dst, const uint16_t* src) {
+  u16x32 line;
+  std::memcpy(&line, src, sizeof(line));
+#if defined(__clang__)
+  __builtin_nontemporal_store(line, reinterpret_cast<u16x32*>(dst));
+#else
+  *reinterpret_cast<u16x32*>(dst) = line;
+#endif
+}
+
 // One contiguous run of n elements: gradients g[0..n), state slots p/m/v
-// (stride 1), parameters out[0..n).
+// (stride 1), parameters out[0..n). The parameters go out a 64-byte line at a
+// time with a non-temporal store: nothing on the host reads them, and a
+// plain store would first read each line into the cache (2 more bytes per
+// element). Measured at the 7.5B shard with 16 threads, the host update took
+// 11.2-12.8 ms against 13.1-14.4 ms with plain stores, with the same results.
 ZERO_HOST_CLONES
 void adam_run(const HostAdam& a, const uint16_t* __restrict g, float* __restrict p, float* __restrict m,
               float* __restrict v, uint16_t* __restrict out, int64_t n) {
-  for (int64_t j = 0; j < n; ++j) {
-    const float gj = widen(g[j]);
-    const float gh = gj * a.coef;
-    const float mg = a.omb1 * gh;
-    const float mj = std::fma(a.beta1, m[j], mg);
-    const float vj = std::fma(a.beta2, v[j], a.omb2 * (gh * gh));
-    const float denom = std::fma(std::sqrt(vj), a.inv_sqrt_bc2, a.eps);
-    const float pd = std::fma(-a.lr_wd, p[j], p[j]);
-    const float pj = std::fma(-a.step_size, mj / denom, pd);
-    if (std::fma(-kCancel, std::fabs(pd), std::fabs(pj)) * denom <
-        (kCancel * a.step_size) * (std::fabs(a.beta1 * m[j]) + std::fabs(mg))) {
-      adam_exact(a, gj, p[j], m[j], v[j]);
-    } else {
-      m[j] = mj;
-      v[j] = vj;
-      p[j] = pj;
-    }
-    out[j] = bf16_rne(p[j]);
+  int64_t j = 0;
+  for (; j < n && (uintptr_t(out + j) & 63u); ++j) out[j] = adam_one(a, g[j], p[j], m[j], v[j]);
+  for (; j + 32 <= n; j += 32) {
+    alignas(64) uint16_t w[32];
+    for (int k = 0; k < 32; ++k) w[k] = adam_one(a, g[j + k], p[j + k], m[j + k], v[j + k]);
+    store_line(out + j, w);
   }
+  for (; j < n; ++j) out[j] = adam_one(a, g[j], p[j], m[j], v[j]);
 }
 
 // Elements [lo, hi) of the shard; g and param hold the call's range, which
