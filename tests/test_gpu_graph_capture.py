@@ -5,7 +5,8 @@ run side by side, one eagerly and one by graph replay; between replays the
 gradients of both are refilled by eager work and the device is synchronised,
 and after every replay each buffer of the graph's shard must equal the eager
 one bit for bit. The step count is a kernel argument, so both use the step
-the graph was captured with."""
+the graph was captured with. The step with the state as three arrays (the
+three-array update, then the unpack) is captured the same way."""
 
 import pytest
 
@@ -24,10 +25,12 @@ def same(a, b):
     return torch.equal(a.view(torch.int64), b.view(torch.int64))
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2-1.5b"])
-def test_graph_replays_equal_eager_steps(name):
+@pytest.mark.parametrize("name,arrays", [("tiny", False), ("gpt2-1.5b", False), ("tiny", True),
+                                         ("gpt2-1.5b", True)],
+                         ids=["tiny", "gpt2-1.5b", "tiny-state-arrays", "gpt2-1.5b-state-arrays"])
+def test_graph_replays_equal_eager_steps(name, arrays):
     wl = synth.WORKLOADS[name]
-    eager, graphed = RankShard(wl), RankShard(wl)
+    eager, graphed = RankShard(wl, state_arrays=arrays), RankShard(wl, state_arrays=arrays)
     torch.cuda.synchronize()
     t = wl.step
     side = torch.cuda.Stream()
@@ -50,7 +53,11 @@ def test_graph_replays_equal_eager_steps(name):
         eager.step(t)
         g.replay()
         torch.cuda.synchronize()
-        assert same(graphed.state, eager.state), (name, rep)
+        if arrays:
+            for k in ("master", "m", "v"):
+                assert same(getattr(graphed, k), getattr(eager, k)), (name, rep, k)
+        else:
+            assert same(graphed.state, eager.state), (name, rep)
         assert same(graphed.param_shard, eager.param_shard), (name, rep)
         assert same(graphed.grad_shard, eager.grad_shard), (name, rep)
         assert same(graphed.rank_sq, eager.rank_sq), (name, rep)
