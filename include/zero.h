@@ -9,7 +9,9 @@
  *   zero_shard_sqnorm   sum of squares of that shard (the rank's share of
  *                       the global gradient norm);
  *   zero_adamw_step     clip with the global norm, AdamW on fp32 master/m/v,
- *                       cast the new master to the bf16 parameter shard;
+ *                       cast the new master to the bf16 parameter shard
+ *                       (the state in the library's tiled buffer;
+ *                       zero_adamw_step_arrays takes three separate arrays);
  *   zero_unpack_params  scatter the bf16 parameter shard back into the
  *                       per-tensor parameters.
  *
